@@ -1,0 +1,205 @@
+/*
+ * tree_attn.h — C ABI of the layout-grounded tree attention library for
+ * AMD Instinct MI355X (gfx950).  Library: libtree_attn.so.
+ *
+ * What is computed.  One document page is a shared prefix X followed by a
+ * layout stream B_1..B_N and content branches Y_1..Y_N.  The layout stream
+ * (with X at its head) is one causal sequence; the tokens of branch Y_k see
+ * X, B_1..B_k and the earlier tokens of Y_k, never another branch (ancestor
+ * sets Anc(B_k) = {X, B_<k}, Anc(Y_k) = {X, B_<=k}: "PaDoc: Layout-Grounded
+ * Parallel Decoding for Document Parsing", paper summary, section "Training
+ * paradigm").  Every call returns exactly softmax(scale * q k^T) v over the
+ * visible keys of each query, with the visible set given per entry point
+ * below.
+ *
+ * Conventions shared by every call.
+ *  - Status: every int-returning call returns TA_OK or a negative TA_ERR_*.
+ *    On error nothing is enqueued, no output is written, and
+ *    tree_attn_last_error() (thread-local) explains.  No exception crosses
+ *    the ABI.
+ *  - Memory: the caller allocates all device memory (tensors, plan workspace,
+ *    scratch).  The library allocates only host memory for plans.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = default
+ *    stream).  Calls only enqueue; none synchronizes the host except
+ *    tree_attn_plan_destroy (waits for the plan's pending upload).  Device
+ *    faults surface at the caller's next synchronization.  Buffers must stay
+ *    alive until the stream has passed the call.
+ *  - Layouts (all contiguous, head_dim fastest, 16-byte aligned):
+ *      q, o : [rows,   Hq,  head_dim]      k, v : [tokens, Hkv, head_dim]
+ *      lse  : [Hq, rows] float32, natural-log log-sum-exp of the scaled
+ *             visible scores (may be NULL).
+ *    GQA: query head h reads KV head h / (Hq / Hkv).
+ *  - dtype: TA_DTYPE_BF16 (bf16 in and out, fp32 accumulation and softmax)
+ *    or TA_DTYPE_F32 (fp32 throughout).  Hq % Hkv == 0, (Hq / Hkv) must
+ *    divide 32, head_dim in {32, 64, 128}, scale > 0 and finite.
+ *  - Sizes are int32; every token or row count must stay below 2^31.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TA_OK 0
+#define TA_ERR_INVALID_ARG (-1) /* malformed description or argument      */
+#define TA_ERR_UNSUPPORTED (-2) /* valid but not built (dtype, head_dim..) */
+#define TA_ERR_CAPACITY (-3)    /* a count overflows int32 / tree > 64     */
+#define TA_ERR_WORKSPACE (-4)   /* workspace or scratch too small/missing  */
+#define TA_ERR_HIP (-5)         /* a HIP runtime call failed               */
+#define TA_ERR_STATE (-6)       /* plan of another kind, or not uploaded   */
+
+#define TA_DTYPE_F32 0
+#define TA_DTYPE_BF16 1
+
+#define TA_PLAN_PREFILL 1
+#define TA_PLAN_DECODE 2
+#define TA_PLAN_VERIFY 3
+
+/* Fields readable with tree_attn_plan_export (all exported as int64). */
+#define TA_FIELD_POSITION 1     /* prefill: [rows] index of the token in its virtual sequence */
+#define TA_FIELD_MAIN_END 2     /* prefill: [rows] visible main keys are [page_base, main_end) */
+#define TA_FIELD_BRANCH_START 3 /* prefill: [rows] visible branch keys are [branch_start, row]; row+1 for main tokens */
+#define TA_FIELD_PAGES 4        /* prefill: [pages][5] base, M = P + sum L, T_page, D, D_seq */
+#define TA_FIELD_BRANCHES 5     /* prefill: [branches][3] main_bound (abs), branch_start (abs), length */
+#define TA_FIELD_DECODE_ROWS 6  /* decode:  [branches][5] main_start, main_len, suffix_start, suffix_len, position */
+#define TA_FIELD_VERIFY_MASK 7  /* verify:  [nodes] ancestor bitmask (bit j: node j of the same branch is an ancestor or itself) */
+#define TA_FIELD_VERIFY_ROWS 8  /* verify:  [nodes][4] ctx_start, ctx_len, tree_base (abs node 0 of the branch), position */
+#define TA_FIELD_WORK 9         /* any:     [work][8] the launch work list (diagnostic; order is not part of the contract) */
+
+typedef struct ta_plan ta_plan; /* opaque, host-owned, immutable once built */
+
+typedef struct ta_plan_info {
+  int32_t kind;             /* TA_PLAN_* */
+  int32_t n_pages;
+  int32_t n_branches;       /* prefill: regions; decode: live branches; verify: trees */
+  int32_t n_work;           /* work items of the main launch (per KV head) */
+  int64_t n_rows;           /* query rows: packed tokens / live branches / draft nodes */
+  int64_t n_keys_a;         /* tokens the first key buffer must hold (k / k_main / k_ctx) */
+  int64_t n_keys_b;         /* tokens the second key buffer must hold (k / k_suffix / k_tree) */
+  int64_t workspace_bytes;  /* device workspace needed by tree_attn_plan_upload */
+  int64_t n_partials;       /* decode: partial (unit, row) slots per query head, else 0 */
+  int64_t visible_pairs;    /* sum over rows of visible keys (algorithmic work, per head) */
+  int64_t max_depth;        /* prefill: max D_PaDoc over pages; verify: max tree depth */
+} ta_plan_info;
+
+/*
+ * Prefill plan: the packed tree-varlen forward ("PaDoc", paper summary,
+ * "Training paradigm": the layout stream is one causal sequence and branch
+ * Y_k queries attend the virtual key/value sequence [X, B_<=k, Y_k]; no dense
+ * mask is stored).
+ *   prefix_len[n_pages]  P of each page (>= 0)
+ *   n_regions[n_pages]   N of each page (>= 0)
+ *   layout_len[sum N]    L_k, page-major (>= 0)
+ *   content_len[sum N]   C_k, page-major (>= 0); a branch-start token, if the
+ *                        model uses one, is counted inside C_k
+ * Packed order of rows and of k/v tokens: per page [X | B_1..B_N | Y_1..Y_N],
+ * pages concatenated.  D and D_seq follow the depth formulas of the same
+ * page, "Formal assumptions and factorization".
+ * Errors: INVALID_ARG for NULL pointers or negative counts, CAPACITY when
+ * the packed length reaches 2^31.  *out is set only on success; free it with
+ * tree_attn_plan_destroy.
+ */
+int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* n_regions,
+                           const int32_t* layout_len, const int32_t* content_len,
+                           int32_t n_pages, ta_plan** out);
+
+/*
+ * Decode plan: one query token per live branch over a main stream stored once
+ * per page (shared-prefix KV reuse: "PaDoc" summary, "Inference"; zero-copy
+ * prefix sharing for forked branches: "HPD-Parsing: Hierarchical Parallel
+ * Document Parsing" notes, "KV cache and shared-prefix reuse").
+ *   prefix_len, n_regions, layout_len: the pages' main streams as above
+ *   br_page[n_branches]     page of each live branch, non-decreasing
+ *   br_region[n_branches]   region k in 1..N of that page
+ *   suffix_len[n_branches]  s_k >= 0 tokens already generated in the branch
+ * Branch b sees main_p[0 : P + L_<=k] and its own s_k + 1 suffix tokens (the
+ * current token's K/V must already be appended).  k_main holds the pages'
+ * main streams concatenated; k_suffix the branches' suffixes concatenated.
+ */
+int tree_attn_plan_decode(const int32_t* prefix_len, const int32_t* n_regions,
+                          const int32_t* layout_len, int32_t n_pages,
+                          const int32_t* br_page, const int32_t* br_region,
+                          const int32_t* suffix_len, int32_t n_branches,
+                          ta_plan** out);
+
+/*
+ * Verify plan: per-branch draft prefix trees under the tree ancestor mask
+ * ("HSD: Training-Free Acceleration for Document Parsing Vision-Language
+ * Models with Hierarchical Speculative Decoding" notes, key design 3 (b),
+ * prefix-tree batching: each draft token sees the accepted sequence and its
+ * own ancestor path).
+ *   ctx_len[n_pages]      accepted context of each page (shared by its branches)
+ *   br_page[n_branches]   page of each tree, non-decreasing
+ *   n_nodes[n_branches]   nodes per tree, 0..64
+ *   parent[sum n_nodes]   per node: -1 (hangs off the context) or an earlier
+ *                         node of the same tree (0 <= parent < own index)
+ * Node i sees its page's whole context plus itself and its ancestors.
+ * Rows and k_tree/v_tree tokens are nodes, tree-major.
+ */
+int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages,
+                          const int32_t* br_page, const int32_t* n_nodes,
+                          const int32_t* parent, int32_t n_branches,
+                          ta_plan** out);
+
+int tree_attn_plan_info(const ta_plan* plan, ta_plan_info* out);
+
+/* Copy an exported field (TA_FIELD_*) into dst[cap]; *n_written = entries
+ * (int64 values) the field holds.  Returns WORKSPACE if cap is too small
+ * (then *n_written still tells the size), INVALID_ARG for a field the plan
+ * kind does not have. */
+int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t* dst,
+                          int64_t cap, int64_t* n_written);
+
+/* Enqueue the asynchronous copy of the plan's device tables into
+ * dev_workspace (>= info.workspace_bytes bytes, 256-byte aligned, caller
+ * owned) on `stream`, and bind the plan to that workspace.  Kernels launched
+ * afterwards read only the workspace.  May be called again to rebind. */
+int tree_attn_plan_upload(ta_plan* plan, void* dev_workspace, size_t bytes, void* stream);
+
+/* Wait for a pending upload, then free the host plan.  NULL is a no-op. */
+void tree_attn_plan_destroy(ta_plan* plan);
+
+/* Scratch bytes tree_attn_decode needs for these head counts. */
+int tree_attn_decode_scratch_bytes(const ta_plan* plan, int32_t hq, int32_t head_dim,
+                                   size_t* bytes);
+
+/* Packed tree-varlen forward over a prefill plan.  q, o: [rows, Hq, d];
+ * k, v: [rows, Hkv, d] (keys are the packed tokens themselves). */
+int tree_attn_prefill(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
+                      int32_t head_dim, float scale, const void* q, const void* k,
+                      const void* v, void* o, float* lse, void* stream);
+
+/* Cascade branch decode over a decode plan: pass 1 streams each page's main
+ * KV once for all of its branches and query heads and each branch's suffix,
+ * writing fp32 partials (m, l, acc) into `scratch`; pass 2 merges them by
+ * log-sum-exp in a fixed order.  q, o: [n_branches, Hq, d];
+ * k_main/v_main: [sum M_p, Hkv, d]; k_suffix/v_suffix: [sum (s_k+1), Hkv, d];
+ * scratch: >= tree_attn_decode_scratch_bytes, 256-byte aligned. */
+int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
+                     int32_t head_dim, float scale, const void* q, const void* k_main,
+                     const void* v_main, const void* k_suffix, const void* v_suffix,
+                     void* o, float* lse, void* scratch, size_t scratch_bytes,
+                     void* stream);
+
+/* Draft-tree verify over a verify plan.  q, o: [nodes, Hq, d];
+ * k_ctx/v_ctx: [sum ctx_len, Hkv, d]; k_tree/v_tree: [nodes, Hkv, d]. */
+int tree_attn_verify(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
+                     int32_t head_dim, float scale, const void* q, const void* k_ctx,
+                     const void* v_ctx, const void* k_tree, const void* v_tree,
+                     void* o, float* lse, void* stream);
+
+/* Message of the last error on this thread ("" if none). */
+const char* tree_attn_last_error(void);
+
+/* Library version string. */
+const char* tree_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

@@ -1,0 +1,196 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared entry
+point, builds plans whose integer fields equal the oracle's plan reference
+exactly, and rejects malformed calls on the host with the documented status
+(nothing is launched, so no GPU is needed)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from tree_structured_attention_amd import binding as ta
+from tree_structured_attention_amd import synth
+
+
+def test_library_exports_every_declared_symbol():
+    L = ta.lib()
+    declared = ta.header_symbols()
+    assert len(declared) == 13
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.tree_attn_version().decode().startswith("tree_attn")
+
+
+# --------------------------------------------------------------------------
+# plan bit-exactness
+# --------------------------------------------------------------------------
+
+def check_prefill_plan(desc):
+    plan = ta.plan_for(desc)
+    ref = oracle.plan_prefill(desc)
+    for f in ("position", "main_end", "branch_start", "pages", "branches"):
+        got = plan.export(f)
+        assert np.array_equal(got, ref[f].reshape(got.shape)), f
+    info = plan.info
+    assert info["n_rows"] == desc.total_tokens()
+    assert info["visible_pairs"] == int((ref["position"] + 1).sum())
+    assert info["max_depth"] == (int(ref["pages"][:, 3].max()) if len(ref["pages"]) else 0)
+    # the work list covers every row exactly once
+    work = plan.export("work")
+    cover = np.zeros(desc.total_tokens(), np.int64)
+    for w in work:
+        cover[w[0]:w[0] + w[1]] += 1
+    assert (cover == 1).all()
+    return plan
+
+
+def test_prefill_plan_configs_exact():
+    for cfg in (1, 2, 3):
+        check_prefill_plan(synth.config(cfg, with_tensors=False).desc)
+
+
+def test_config1_golden_depth_through_library():
+    plan = ta.plan_for(synth.config1(with_tensors=False).desc)
+    pages = plan.export("pages")
+    assert pages.tolist() == [[0, 64 + 18, 128, 31, 64]]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_prefill_plan_random_exact(seed):
+    rng = np.random.default_rng(1000 + seed)
+    n_pages = int(rng.integers(1, 4))
+    P = rng.integers(0, 70, n_pages)
+    N = rng.integers(0, 6, n_pages)
+    L = [rng.integers(0, 5, n) for n in N]
+    C = [rng.integers(0, 90, n) for n in N]
+    desc = synth.make_prefill_desc(P, L, C)
+    check_prefill_plan(desc)
+
+
+def test_prefill_plan_edge_descriptions():
+    for P, L, C in [(0, [0], [1]), (1, [], []), (0, [3, 0], [0, 0]), (64, [0, 0, 0], [64, 128, 1]),
+                    (63, [1], [65])]:
+        check_prefill_plan(synth.make_prefill_desc([P], [np.array(L)], [np.array(C)]))
+
+
+def test_decode_plan_exact():
+    for w in (synth.config4(with_tensors=False), synth.config4(with_tensors=False, n_pages=3, seed=9)):
+        plan = ta.plan_for(w.desc)
+        ref = oracle.plan_decode(w.desc)
+        assert np.array_equal(plan.export("decode_rows"), ref["rows"])
+        info = plan.info
+        assert info["n_keys_a"] == int(w.desc.main_tokens().sum())
+        assert info["n_keys_b"] == w.desc.suffix_tokens()
+
+
+def test_verify_plan_exact():
+    for w in (synth.config5(with_tensors=False), synth.config5(with_tensors=False, n_pages=3, seed=5)):
+        plan = ta.plan_for(w.desc)
+        ref = oracle.plan_verify(w.desc)
+        assert np.array_equal(plan.export("verify_mask").astype(np.uint64), ref["mask"])
+        assert np.array_equal(plan.export("verify_rows"), ref["rows"])
+    # depth bound of the generator: no node deeper than 8 below the context
+    assert plan.info["max_depth"] <= 8
+
+
+def test_verify_plan_64_node_tree_uses_top_bit():
+    parent = np.arange(-1, 63, dtype=np.int32)  # a chain of 64 nodes
+    desc = synth.VerifyDesc(np.array([5], np.int32), np.array([0], np.int32), np.array([64], np.int32), parent)
+    plan = ta.plan_for(desc)
+    m = plan.export("verify_mask").astype(np.uint64)
+    assert int(m[-1]) == (1 << 64) - 1
+    assert np.array_equal(m, oracle.plan_verify(desc)["mask"])
+
+
+# --------------------------------------------------------------------------
+# host-side error paths
+# --------------------------------------------------------------------------
+
+def expect(code, fn, *a, **k):
+    with pytest.raises(ta.TreeAttnError) as e:
+        fn(*a, **k)
+    assert e.value.code == code, str(e.value)
+
+
+def test_plan_errors():
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_prefill, [-1], [0], [], [])
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_prefill, [4], [1], [-2], [3])
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_prefill, [4], [1], [2], [-3])
+    expect(ta.TA_ERR_CAPACITY, ta.plan_prefill, [2**30, 2**30], [0, 0], [], [])
+    # decode: region out of range, pages not grouped, negative suffix
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_decode, [4], [2], [1, 1], [0], [3], [0])
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_decode, [4, 4], [1, 1], [1, 1], [1, 0], [1, 1], [0, 0])
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_decode, [4], [1], [1], [0], [1], [-1])
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_decode, [4], [1], [1], [1], [1], [0])
+    # verify: parent not earlier, too many nodes, bad page
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_verify, [5], [0], [3], [-1, 2, 0])
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_verify, [5], [0], [2], [-1, 1])
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_verify, [5], [0], [2], [-2, 0])
+    expect(ta.TA_ERR_CAPACITY, ta.plan_verify, [5], [0], [65], [-1] * 65)
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_verify, [5], [1], [1], [-1])
+
+
+class FakeArgs:
+    """Aligned host addresses standing in for device pointers: every call
+    below fails validation before anything dereferences them."""
+
+    def __init__(self):
+        self.buf = (ctypes.c_uint8 * 4096)()
+        base = ctypes.addressof(self.buf)
+        self.p = ctypes.c_void_p((base + 255) & ~255)
+        self.odd = ctypes.c_void_p(((base + 255) & ~255) + 8)
+
+
+def test_launch_errors_before_any_device_work():
+    L = ta.lib()
+    fa = FakeArgs()
+    p = fa.p
+    plan = ta.plan_prefill([8], [1], [2], [3])
+    h = plan.handle
+    bf, f32 = ta.TA_DTYPE_BF16, ta.TA_DTYPE_F32
+    # (dtype, hq, hkv, d, scale) -> status
+    cases = [
+        ((7, 2, 1, 32, 0.2), ta.TA_ERR_UNSUPPORTED),
+        ((bf, 3, 2, 32, 0.2), ta.TA_ERR_INVALID_ARG),
+        ((bf, 0, 1, 32, 0.2), ta.TA_ERR_INVALID_ARG),
+        ((bf, 6, 1, 32, 0.2), ta.TA_ERR_UNSUPPORTED),   # group 6 does not divide 32
+        ((bf, 2, 1, 96, 0.2), ta.TA_ERR_UNSUPPORTED),
+        ((bf, 2, 1, 32, 0.0), ta.TA_ERR_INVALID_ARG),
+        ((bf, 2, 1, 32, float("nan")), ta.TA_ERR_INVALID_ARG),
+        ((f32, 2, 1, 32, 0.2), ta.TA_ERR_STATE),        # valid, but never uploaded
+    ]
+    for (dt, hq, hkv, d, sc), code in cases:
+        rc = L.tree_attn_prefill(h, dt, hq, hkv, d, sc, p, p, p, p, None, None)
+        assert rc == code, (dt, hq, hkv, d, sc, rc, ta.last_error())
+    # NULL and misaligned tensors
+    assert L.tree_attn_prefill(h, bf, 2, 1, 32, 0.2, None, p, p, p, None, None) == ta.TA_ERR_INVALID_ARG
+    assert L.tree_attn_prefill(h, bf, 2, 1, 32, 0.2, fa.odd, p, p, p, None, None) == ta.TA_ERR_INVALID_ARG
+    # wrong plan kind for the entry point
+    assert L.tree_attn_verify(h, bf, 2, 1, 32, 0.2, p, p, p, p, p, p, None, None) == ta.TA_ERR_STATE
+    # workspace checks of upload happen before any copy
+    assert L.tree_attn_plan_upload(h, None, 1 << 20, None) == ta.TA_ERR_WORKSPACE
+    assert L.tree_attn_plan_upload(h, fa.odd, 1 << 20, None) == ta.TA_ERR_INVALID_ARG
+    assert L.tree_attn_plan_upload(h, p, 16, None) == ta.TA_ERR_WORKSPACE
+
+
+def test_decode_scratch_errors():
+    L = ta.lib()
+    fa = FakeArgs()
+    p = fa.p
+    plan = ta.plan_decode([10], [2], [1, 1], [0, 0], [1, 2], [3, 0])
+    need = ta.decode_scratch_bytes(plan, 4, 32)
+    assert need > 0
+    bf = ta.TA_DTYPE_BF16
+    rc = L.tree_attn_decode(plan.handle, bf, 4, 2, 32, 0.2, p, p, p, p, p, p, None, None, need, None)
+    assert rc == ta.TA_ERR_WORKSPACE
+    rc = L.tree_attn_decode(plan.handle, bf, 4, 2, 32, 0.2, p, p, p, p, p, p, None, p, need - 1, None)
+    assert rc == ta.TA_ERR_WORKSPACE
+    rc = L.tree_attn_decode(plan.handle, bf, 4, 2, 32, 0.2, p, p, p, p, p, p, None, p, need, None)
+    assert rc == ta.TA_ERR_STATE
+
+
+def test_export_errors():
+    plan = ta.plan_prefill([8], [1], [2], [3])
+    with pytest.raises(ta.TreeAttnError) as e:
+        ta.plan_export(plan, "verify_mask")
+    assert e.value.code == ta.TA_ERR_INVALID_ARG

@@ -1,0 +1,336 @@
+"""Thin ctypes binding over libtree_attn's C ABI (argument marshalling only).
+
+Every step of the attention path runs in the HIP library; this module only
+turns torch tensors into pointers and streams, allocates the caller-owned
+device workspace/scratch with torch, and raises on a non-zero status.  It
+fails loudly if the library has not been built: there is no fallback.
+
+Names mirror the C entry points without the ``tree_attn_`` prefix:
+``plan_prefill``, ``plan_decode``, ``plan_verify``, ``plan_info``,
+``plan_export``, ``plan_upload``, ``plan_destroy``, ``decode_scratch_bytes``,
+``prefill``, ``decode``, ``verify``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import Optional
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtree_attn.so")
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tree_attn.h")
+
+TA_OK = 0
+TA_ERR_INVALID_ARG = -1
+TA_ERR_UNSUPPORTED = -2
+TA_ERR_CAPACITY = -3
+TA_ERR_WORKSPACE = -4
+TA_ERR_HIP = -5
+TA_ERR_STATE = -6
+
+TA_DTYPE_F32 = 0
+TA_DTYPE_BF16 = 1
+
+TA_PLAN_PREFILL = 1
+TA_PLAN_DECODE = 2
+TA_PLAN_VERIFY = 3
+
+FIELD = {
+    "position": 1,
+    "main_end": 2,
+    "branch_start": 3,
+    "pages": 4,
+    "branches": 5,
+    "decode_rows": 6,
+    "verify_mask": 7,
+    "verify_rows": 8,
+    "work": 9,
+}
+FIELD_WIDTH = {"pages": 5, "branches": 3, "decode_rows": 5, "verify_rows": 4, "work": 8}
+
+
+class TreeAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"tree_attn error {code}: {msg}")
+        self.code = code
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("n_pages", ctypes.c_int32),
+        ("n_branches", ctypes.c_int32),
+        ("n_work", ctypes.c_int32),
+        ("n_rows", ctypes.c_int64),
+        ("n_keys_a", ctypes.c_int64),
+        ("n_keys_b", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
+        ("n_partials", ctypes.c_int64),
+        ("visible_pairs", ctypes.c_int64),
+        ("max_depth", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtree_attn.so (built by tree_structured_attention_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m tree_structured_attention_amd.build` "
+                "(the tree attention path has no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        pp = ctypes.POINTER(ctypes.c_void_p)
+        sig = {
+            "tree_attn_plan_prefill": ([_I32P, _I32P, _I32P, _I32P, i32, pp], ctypes.c_int),
+            "tree_attn_plan_decode": ([_I32P, _I32P, _I32P, i32, _I32P, _I32P, _I32P, i32, pp], ctypes.c_int),
+            "tree_attn_plan_verify": ([_I32P, i32, _I32P, _I32P, _I32P, i32, pp], ctypes.c_int),
+            "tree_attn_plan_info": ([_P, ctypes.POINTER(PlanInfo)], ctypes.c_int),
+            "tree_attn_plan_export": ([_P, i32, ctypes.POINTER(i64), i64, ctypes.POINTER(i64)], ctypes.c_int),
+            "tree_attn_plan_upload": ([_P, _P, sz, _P], ctypes.c_int),
+            "tree_attn_plan_destroy": ([_P], None),
+            "tree_attn_decode_scratch_bytes": ([_P, i32, i32, ctypes.POINTER(sz)], ctypes.c_int),
+            "tree_attn_prefill": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+            "tree_attn_decode": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
+                                 ctypes.c_int),
+            "tree_attn_verify": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+            "tree_attn_last_error": ([], ctypes.c_char_p),
+            "tree_attn_version": ([], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Entry points declared in include/tree_attn.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(tree_attn_\w+)\s*\(", text)))
+
+
+def last_error() -> str:
+    return lib().tree_attn_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != TA_OK:
+        raise TreeAttnError(rc, last_error())
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_I32P) if a.size else None
+
+
+# ---------------------------------------------------------------------------
+# plans
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """Owns a host plan (and, once uploaded, its device workspace tensor)."""
+
+    def __init__(self, handle: int, kind: int):
+        self.handle = ctypes.c_void_p(handle)
+        self.kind = kind
+        self.workspace: Optional[torch.Tensor] = None
+        self._keep = []
+
+    @property
+    def info(self) -> dict:
+        return plan_info(self)
+
+    def export(self, field: str) -> np.ndarray:
+        return plan_export(self, field)
+
+    def upload(self, device=None, stream=None) -> "Plan":
+        return plan_upload(self, device, stream)
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            lib().tree_attn_plan_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
+
+
+def plan_prefill(prefix_len, n_regions, layout_len, content_len) -> Plan:
+    P, N, L, C = _i32(prefix_len), _i32(n_regions), _i32(layout_len), _i32(content_len)
+    out = ctypes.c_void_p()
+    _check(lib().tree_attn_plan_prefill(_ptr(P), _ptr(N), _ptr(L), _ptr(C), int(P.size), ctypes.byref(out)))
+    return Plan(out.value, TA_PLAN_PREFILL)
+
+
+def plan_decode(prefix_len, n_regions, layout_len, br_page, br_region, suffix_len) -> Plan:
+    P, N, L = _i32(prefix_len), _i32(n_regions), _i32(layout_len)
+    bp, br, s = _i32(br_page), _i32(br_region), _i32(suffix_len)
+    out = ctypes.c_void_p()
+    _check(lib().tree_attn_plan_decode(_ptr(P), _ptr(N), _ptr(L), int(P.size), _ptr(bp), _ptr(br), _ptr(s),
+                                       int(bp.size), ctypes.byref(out)))
+    return Plan(out.value, TA_PLAN_DECODE)
+
+
+def plan_verify(ctx_len, br_page, n_nodes, parent) -> Plan:
+    c, bp, nn, pa = _i32(ctx_len), _i32(br_page), _i32(n_nodes), _i32(parent)
+    out = ctypes.c_void_p()
+    _check(lib().tree_attn_plan_verify(_ptr(c), int(c.size), _ptr(bp), _ptr(nn), _ptr(pa), int(bp.size),
+                                       ctypes.byref(out)))
+    return Plan(out.value, TA_PLAN_VERIFY)
+
+
+def plan_for(desc) -> Plan:
+    """Plan from a synth description object (PrefillDesc / DecodeDesc / VerifyDesc)."""
+    name = type(desc).__name__
+    if name == "PrefillDesc":
+        return plan_prefill(desc.prefix_len, desc.n_regions, desc.layout_len, desc.content_len)
+    if name == "DecodeDesc":
+        return plan_decode(desc.prefix_len, desc.n_regions, desc.layout_len, desc.br_page, desc.br_region,
+                           desc.suffix_len)
+    if name == "VerifyDesc":
+        return plan_verify(desc.ctx_len, desc.br_page, desc.n_nodes, desc.parent)
+    raise TypeError(f"no plan for {name}")
+
+
+def plan_info(plan: Plan) -> dict:
+    info = PlanInfo()
+    _check(lib().tree_attn_plan_info(plan.handle, ctypes.byref(info)))
+    return info.as_dict()
+
+
+def plan_export(plan: Plan, field: str) -> np.ndarray:
+    n = ctypes.c_int64()
+    rc = lib().tree_attn_plan_export(plan.handle, FIELD[field], None, 0, ctypes.byref(n))
+    if rc not in (TA_OK, TA_ERR_WORKSPACE):
+        _check(rc)
+    buf = np.zeros(max(n.value, 1), dtype=np.int64)
+    _check(lib().tree_attn_plan_export(plan.handle, FIELD[field], buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                       buf.size, ctypes.byref(n)))
+    buf = buf[: n.value]
+    w = FIELD_WIDTH.get(field)
+    return buf.reshape(-1, w) if w else buf
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def plan_upload(plan: Plan, device=None, stream=None) -> Plan:
+    """Allocate the device workspace with torch and enqueue the plan copy."""
+    nbytes = plan_info(plan)["workspace_bytes"]
+    dev = torch.device("cuda" if device is None else device)
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    off = (-ws.data_ptr()) % 256
+    ws_view = ws[off: off + nbytes]
+    _check(lib().tree_attn_plan_upload(plan.handle, ctypes.c_void_p(ws_view.data_ptr()), nbytes,
+                                       _stream_handle(stream)))
+    plan.workspace = ws
+    return plan
+
+
+def plan_destroy(plan: Plan):
+    plan.close()
+
+
+def decode_scratch_bytes(plan: Plan, hq: int, head_dim: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().tree_attn_decode_scratch_bytes(plan.handle, hq, head_dim, ctypes.byref(n)))
+    return int(n.value)
+
+
+# ---------------------------------------------------------------------------
+# launches
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return TA_DTYPE_F32
+    raise TreeAttnError(TA_ERR_UNSUPPORTED, f"dtype {t.dtype} is not supported (bf16 or fp32)")
+
+
+def _dev_ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TreeAttnError(TA_ERR_INVALID_ARG, "tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise TreeAttnError(TA_ERR_INVALID_ARG, "tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _heads(q: torch.Tensor, k: torch.Tensor):
+    if q.dim() != 3 or k.dim() != 3:
+        raise TreeAttnError(TA_ERR_INVALID_ARG, "q is [rows, Hq, d] and k/v are [tokens, Hkv, d]")
+    return q.shape[1], k.shape[1], q.shape[2]
+
+
+def _outputs(q, want_lse, out=None, lse=None):
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    return out, (lse if want_lse else None)
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def prefill(plan: Plan, q, k, v, scale=None, want_lse=True, out=None, lse=None, stream=None):
+    hq, hkv, d = _heads(q, k)
+    o, l = _outputs(q, want_lse, out, lse)
+    _check(lib().tree_attn_prefill(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
+                                   _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(l), _stream_handle(stream)))
+    return o, l
+
+
+def decode(plan: Plan, q, k_main, v_main, k_suffix, v_suffix, scale=None, want_lse=True, out=None, lse=None,
+           scratch: Optional[torch.Tensor] = None, stream=None):
+    hq, hkv, d = _heads(q, k_main)
+    o, l = _outputs(q, want_lse, out, lse)
+    need = decode_scratch_bytes(plan, hq, d)
+    if scratch is None:
+        scratch = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    off = (-scratch.data_ptr()) % 256
+    sview = scratch[off:]
+    _check(lib().tree_attn_decode(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
+                                  _dev_ptr(k_main), _dev_ptr(v_main), _dev_ptr(k_suffix), _dev_ptr(v_suffix),
+                                  _dev_ptr(o), _dev_ptr(l), ctypes.c_void_p(sview.data_ptr()), sview.numel(),
+                                  _stream_handle(stream)))
+    return o, l
+
+
+def verify(plan: Plan, q, k_ctx, v_ctx, k_tree, v_tree, scale=None, want_lse=True, out=None, lse=None,
+           stream=None):
+    hq, hkv, d = _heads(q, k_ctx)
+    o, l = _outputs(q, want_lse, out, lse)
+    _check(lib().tree_attn_verify(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
+                                  _dev_ptr(k_ctx), _dev_ptr(v_ctx), _dev_ptr(k_tree), _dev_ptr(v_tree),
+                                  _dev_ptr(o), _dev_ptr(l), _stream_handle(stream)))
+    return o, l

@@ -1,0 +1,268 @@
+// C ABI of libtree_attn: argument validation, plan accessors and launches.
+// Every check runs on the host before anything is enqueued, so an invalid
+// call leaves outputs and the stream untouched.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "ta_kernels.h"
+
+namespace ta {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_heads(int32_t dtype, int32_t hq, int32_t hkv, int32_t d, float scale) {
+  if (dtype != TA_DTYPE_BF16 && dtype != TA_DTYPE_F32) return fail(TA_ERR_UNSUPPORTED, "dtype must be TA_DTYPE_BF16 or TA_DTYPE_F32");
+  if (hq <= 0 || hkv <= 0) return fail(TA_ERR_INVALID_ARG, "hq and hkv must be positive");
+  if (hq % hkv != 0) return fail(TA_ERR_INVALID_ARG, "hq must be a multiple of hkv");
+  const int g = hq / hkv;
+  if (32 % g != 0) return fail(TA_ERR_UNSUPPORTED, "hq / hkv must divide 32");
+  if (d != 32 && d != 64 && d != 128) return fail(TA_ERR_UNSUPPORTED, "head_dim must be 32, 64 or 128");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(TA_ERR_INVALID_ARG, "scale must be positive and finite");
+  return TA_OK;
+}
+
+int check_tensor(const void* ptr, int64_t count, const char* name) {
+  if (count == 0) return TA_OK;
+  if (!ptr) return fail(TA_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned(ptr, 16)) return fail(TA_ERR_INVALID_ARG, std::string(name) + " must be 16-byte aligned");
+  return TA_OK;
+}
+
+int check_plan(const ta_plan* plan, int kind, const char* who) {
+  if (!plan) return fail(TA_ERR_INVALID_ARG, std::string(who) + ": plan is NULL");
+  if (plan->kind != kind) return fail(TA_ERR_STATE, std::string(who) + ": plan was built for another entry point");
+  return TA_OK;
+}
+
+int check_uploaded(const ta_plan* plan, const char* who) {
+  if (!plan->dev) return fail(TA_ERR_STATE, std::string(who) + ": plan is not uploaded (tree_attn_plan_upload)");
+  return TA_OK;
+}
+
+AttnParams base_params(const ta_plan* plan, int32_t hq, int32_t hkv, float scale) {
+  AttnParams p{};
+  const unsigned char* dev = static_cast<const unsigned char*>(plan->dev);
+  p.work = reinterpret_cast<const WorkItem*>(dev + plan->layout.work);
+  p.row_a = reinterpret_cast<const int32_t*>(dev + plan->layout.row_a);
+  p.row_b = reinterpret_cast<const int32_t*>(dev + plan->layout.row_b);
+  p.row_mask = reinterpret_cast<const uint64_t*>(dev + plan->layout.mask);
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  p.c = scale * 1.4426950408889634f;
+  p.n_rows = plan->n_rows;
+  return p;
+}
+
+int hip_status(hipError_t e, const char* who) {
+  if (e == hipSuccess) return TA_OK;
+  return fail(TA_ERR_HIP, std::string(who) + ": " + hipGetErrorString(e));
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+int64_t decode_scratch(const ta_plan* plan, int32_t hq, int32_t d) {
+  const int64_t slots = plan->n_partials * hq;
+  return align256(slots * d * 4) + align256(slots * 2 * 4);
+}
+
+}  // namespace
+}  // namespace ta
+
+using namespace ta;
+
+extern "C" const char* tree_attn_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" const char* tree_attn_version(void) { return "tree_attn 0.1 gfx950"; }
+
+extern "C" int tree_attn_plan_info(const ta_plan* plan, ta_plan_info* out) {
+  if (!plan || !out) return fail(TA_ERR_INVALID_ARG, "plan_info: NULL argument");
+  out->kind = plan->kind;
+  out->n_pages = plan->n_pages;
+  out->n_branches = plan->n_branches;
+  out->n_work = int32_t(plan->work.size());
+  out->n_rows = plan->n_rows;
+  out->n_keys_a = plan->n_keys_a;
+  out->n_keys_b = plan->n_keys_b;
+  out->workspace_bytes = plan->layout.total;
+  out->n_partials = plan->n_partials;
+  out->visible_pairs = plan->visible_pairs;
+  out->max_depth = plan->max_depth;
+  return TA_OK;
+}
+
+extern "C" int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t* dst, int64_t cap,
+                                     int64_t* n_written) {
+  if (!plan || !n_written) return fail(TA_ERR_INVALID_ARG, "plan_export: NULL argument");
+  std::vector<int64_t> work_tmp;
+  const std::vector<int64_t>* src = nullptr;
+  const int k = plan->kind;
+  switch (field) {
+    case TA_FIELD_POSITION: if (k == TA_PLAN_PREFILL) src = &plan->position; break;
+    case TA_FIELD_MAIN_END: if (k == TA_PLAN_PREFILL) src = &plan->main_end; break;
+    case TA_FIELD_BRANCH_START: if (k == TA_PLAN_PREFILL) src = &plan->branch_start; break;
+    case TA_FIELD_PAGES: if (k == TA_PLAN_PREFILL) src = &plan->pages5; break;
+    case TA_FIELD_BRANCHES: if (k == TA_PLAN_PREFILL) src = &plan->branches3; break;
+    case TA_FIELD_DECODE_ROWS: if (k == TA_PLAN_DECODE) src = &plan->decode_rows5; break;
+    case TA_FIELD_VERIFY_MASK: if (k == TA_PLAN_VERIFY) src = &plan->verify_mask; break;
+    case TA_FIELD_VERIFY_ROWS: if (k == TA_PLAN_VERIFY) src = &plan->verify_rows4; break;
+    case TA_FIELD_WORK:
+      for (const WorkItem& w : plan->work)
+        work_tmp.insert(work_tmp.end(), {w.row0, w.nrows, w.a_lo, w.a_full, w.a_hi, w.b_lo, w.b_hi, w.out});
+      src = &work_tmp;
+      break;
+    default: break;
+  }
+  if (!src) return fail(TA_ERR_INVALID_ARG, "plan_export: field not available for this plan kind");
+  *n_written = int64_t(src->size());
+  if (cap < int64_t(src->size())) return fail(TA_ERR_WORKSPACE, "plan_export: destination too small");
+  if (!src->empty()) {
+    if (!dst) return fail(TA_ERR_INVALID_ARG, "plan_export: dst is NULL");
+    std::memcpy(dst, src->data(), src->size() * sizeof(int64_t));
+  }
+  return TA_OK;
+}
+
+extern "C" int tree_attn_plan_upload(ta_plan* plan, void* dev_workspace, size_t bytes, void* stream) {
+  if (!plan) return fail(TA_ERR_INVALID_ARG, "plan_upload: plan is NULL");
+  if (!dev_workspace) return fail(TA_ERR_WORKSPACE, "plan_upload: workspace is NULL");
+  if (!aligned(dev_workspace, 256)) return fail(TA_ERR_INVALID_ARG, "plan_upload: workspace must be 256-byte aligned");
+  if (int64_t(bytes) < plan->layout.total) return fail(TA_ERR_WORKSPACE, "plan_upload: workspace smaller than workspace_bytes");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (!plan->upload_event) {
+    hipEvent_t ev = nullptr;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_status(e, "plan_upload");
+    plan->upload_event = ev;
+  }
+  e = hipMemcpyAsync(dev_workspace, plan->blob.data(), plan->blob.size(), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_status(e, "plan_upload");
+  e = hipEventRecord(static_cast<hipEvent_t>(plan->upload_event), st);
+  if (e != hipSuccess) return hip_status(e, "plan_upload");
+  plan->dev = dev_workspace;
+  return TA_OK;
+}
+
+extern "C" void tree_attn_plan_destroy(ta_plan* plan) {
+  if (!plan) return;
+  if (plan->upload_event) {
+    hipEventSynchronize(static_cast<hipEvent_t>(plan->upload_event));
+    hipEventDestroy(static_cast<hipEvent_t>(plan->upload_event));
+  }
+  delete plan;
+}
+
+extern "C" int tree_attn_decode_scratch_bytes(const ta_plan* plan, int32_t hq, int32_t head_dim, size_t* bytes) {
+  if (!plan || !bytes) return fail(TA_ERR_INVALID_ARG, "decode_scratch_bytes: NULL argument");
+  if (plan->kind != TA_PLAN_DECODE) return fail(TA_ERR_STATE, "decode_scratch_bytes: not a decode plan");
+  if (hq <= 0 || head_dim <= 0) return fail(TA_ERR_INVALID_ARG, "decode_scratch_bytes: hq and head_dim must be positive");
+  *bytes = size_t(decode_scratch(plan, hq, head_dim));
+  return TA_OK;
+}
+
+extern "C" int tree_attn_prefill(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim,
+                                 float scale, const void* q, const void* k, const void* v, void* o, float* lse,
+                                 void* stream) {
+  int rc = check_plan(plan, TA_PLAN_PREFILL, "prefill");
+  if (rc) return rc;
+  if ((rc = check_heads(dtype, hq, hkv, head_dim, scale))) return rc;
+  const int64_t rows = plan->n_rows;
+  if ((rc = check_tensor(q, rows, "q")) || (rc = check_tensor(k, rows, "k")) || (rc = check_tensor(v, rows, "v")) ||
+      (rc = check_tensor(o, rows, "o")))
+    return rc;
+  if (lse && !aligned(lse, 4)) return fail(TA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if ((rc = check_uploaded(plan, "prefill"))) return rc;
+  AttnParams p = base_params(plan, hq, hkv, scale);
+  p.q = q;
+  p.ka = p.kb = k;
+  p.va = p.vb = v;
+  p.o = o;
+  p.lse = lse;
+  return hip_status(launch_attention(kPrefill, dtype, p, int(plan->work.size()), head_dim, static_cast<hipStream_t>(stream)),
+                    "prefill launch");
+}
+
+extern "C" int tree_attn_verify(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim,
+                                float scale, const void* q, const void* k_ctx, const void* v_ctx, const void* k_tree,
+                                const void* v_tree, void* o, float* lse, void* stream) {
+  int rc = check_plan(plan, TA_PLAN_VERIFY, "verify");
+  if (rc) return rc;
+  if ((rc = check_heads(dtype, hq, hkv, head_dim, scale))) return rc;
+  const int64_t rows = plan->n_rows;
+  if ((rc = check_tensor(q, rows, "q")) || (rc = check_tensor(k_ctx, plan->n_keys_a, "k_ctx")) ||
+      (rc = check_tensor(v_ctx, plan->n_keys_a, "v_ctx")) || (rc = check_tensor(k_tree, rows, "k_tree")) ||
+      (rc = check_tensor(v_tree, rows, "v_tree")) || (rc = check_tensor(o, rows, "o")))
+    return rc;
+  if (lse && !aligned(lse, 4)) return fail(TA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if ((rc = check_uploaded(plan, "verify"))) return rc;
+  AttnParams p = base_params(plan, hq, hkv, scale);
+  p.q = q;
+  p.ka = k_ctx;
+  p.va = v_ctx;
+  p.kb = k_tree;
+  p.vb = v_tree;
+  p.o = o;
+  p.lse = lse;
+  return hip_status(launch_attention(kVerify, dtype, p, int(plan->work.size()), head_dim, static_cast<hipStream_t>(stream)),
+                    "verify launch");
+}
+
+extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim,
+                                float scale, const void* q, const void* k_main, const void* v_main,
+                                const void* k_suffix, const void* v_suffix, void* o, float* lse, void* scratch,
+                                size_t scratch_bytes, void* stream) {
+  int rc = check_plan(plan, TA_PLAN_DECODE, "decode");
+  if (rc) return rc;
+  if ((rc = check_heads(dtype, hq, hkv, head_dim, scale))) return rc;
+  const int64_t rows = plan->n_rows;
+  if ((rc = check_tensor(q, rows, "q")) || (rc = check_tensor(k_main, plan->n_keys_a, "k_main")) ||
+      (rc = check_tensor(v_main, plan->n_keys_a, "v_main")) || (rc = check_tensor(k_suffix, plan->n_keys_b, "k_suffix")) ||
+      (rc = check_tensor(v_suffix, plan->n_keys_b, "v_suffix")) || (rc = check_tensor(o, rows, "o")))
+    return rc;
+  if (lse && !aligned(lse, 4)) return fail(TA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const int64_t need = decode_scratch(plan, hq, head_dim);
+  if (rows > 0) {
+    if (!scratch) return fail(TA_ERR_WORKSPACE, "decode: scratch is NULL");
+    if (!aligned(scratch, 256)) return fail(TA_ERR_INVALID_ARG, "decode: scratch must be 256-byte aligned");
+    if (int64_t(scratch_bytes) < need) return fail(TA_ERR_WORKSPACE, "decode: scratch smaller than tree_attn_decode_scratch_bytes");
+  }
+  if ((rc = check_uploaded(plan, "decode"))) return rc;
+  AttnParams p = base_params(plan, hq, hkv, scale);
+  p.q = q;
+  p.ka = k_main;
+  p.va = v_main;
+  p.kb = k_suffix;
+  p.vb = v_suffix;
+  p.o = o;
+  p.lse = lse;
+  const int64_t slots = plan->n_partials * hq;
+  p.part_acc = static_cast<float*>(scratch);
+  p.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(scratch) + align256(slots * head_dim * 4));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = hip_status(launch_attention(kDecode, dtype, p, int(plan->work.size()), head_dim, st), "decode launch");
+  if (rc) return rc;
+  MergeParams m{};
+  m.merge = reinterpret_cast<const MergeRow*>(static_cast<const unsigned char*>(plan->dev) + plan->layout.merge);
+  m.part_acc = p.part_acc;
+  m.part_ml = p.part_ml;
+  m.o = o;
+  m.lse = lse;
+  m.n_rows = int32_t(rows);
+  m.hq = hq;
+  return hip_status(launch_merge(dtype, m, head_dim, st), "decode merge launch");
+}

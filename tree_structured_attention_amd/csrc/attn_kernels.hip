@@ -1,0 +1,541 @@
+// HIP kernels for layout-grounded tree attention on gfx950 (MI355X).
+//
+// One kernel template serves the three entry points.  A workgroup takes one
+// work item (a tile of up to 64 query tokens, times the query heads of one
+// KV head that it owns) and walks two key segments tile by tile:
+//   prefill  seg A = the page's main stream [X | B] (per-row upper bound),
+//            seg B = the content branches overlapping the tile (per-row
+//            branch-causal interval)         -- PaDoc summary, "Training
+//            paradigm": branch Y_k attends [X, B_<=k, Y_k]
+//   verify   seg A = the page's accepted context (all visible),
+//            seg B = the tile's draft-tree nodes (per-row ancestor bitmask)
+//                                            -- HSD notes, key design 3 (b)
+//   decode   seg A = one chunk of a page's main stream, shared by every live
+//            branch and query head of the page (per-row bound P + L_<=k), or
+//            seg B = one chunk of one branch's own suffix; the kernel writes
+//            fp32 partials that a second kernel merges by log-sum-exp
+//                                            -- PaDoc summary, "Inference";
+//            HPD-Parsing notes, shared-prefix KV reuse
+//
+// MFMA formulation (wave64, one wave = 32 query rows):
+//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q
+//   held in registers, so each lane owns one query row (lane % 32) and the
+//   row's softmax statistics live in two lanes (lane, lane + 32).
+//   O^T += V^T P^T: A = V^T read from a transposed LDS tile, B = P^T taken
+//   straight from the S^T accumulators, so P never leaves registers.
+//   K rows are loaded in a permuted order (bits 2 and 3 of the MFMA row index
+//   swapped) so that the 8 keys a lane holds for the PV step are contiguous.
+// Softmax is online in fp32 with exp2 and the scale folded into one FMA; the
+// running rescale is skipped when no row of the wave raised its maximum.
+// Non-visible scores are replaced by -inf (selection), padded keys are
+// zero-filled, so no value outside a row's ancestors can reach its output
+// unless it is a non-finite V of a key another row of the same tile needs.
+// fp32 inputs use v_mfma_f32_32x32x2f32 with the same tiling (no
+// down-conversion).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "ta_kernels.h"
+
+namespace ta {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float shfl_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// MFMA row m of a 32-key block holds physical key pi(m): bits 2 and 3 swapped.
+__device__ __forceinline__ int key_perm(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+// Accumulator register i of a lane in half h holds (within the 32-key block)
+// physical key 16 * (i / 8) + 8 * h + (i % 8).
+__device__ __forceinline__ int reg_key(int i, int h) { return 16 * (i >> 3) + 8 * h + (i & 7); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
+  return uint32_t(__builtin_bit_cast(uint16_t, x)) | (uint32_t(__builtin_bit_cast(uint16_t, y)) << 16);
+}
+
+template <typename T>
+struct TileCfg;
+
+template <>
+struct TileCfg<__bf16> {
+  static constexpr int kElt = 2;
+};
+template <>
+struct TileCfg<float> {
+  static constexpr int kElt = 4;
+};
+
+// LDS geometry for one 64-key tile of head_dim D.
+template <typename T, int D>
+struct Lds {
+  static constexpr bool kBf = std::is_same<T, __bf16>::value;
+  // K tile row-major [64][D] with a 16-byte pad per row.
+  static constexpr int kKRow = D * TileCfg<T>::kElt + 16;
+  static constexpr int kKBytes = kKeyTile * kKRow;
+  // V tile: bf16 transposed [D][64] (+16 B pad); fp32 row-major [64][D] (+16 B).
+  static constexpr int kVRow = kBf ? (kKeyTile * 2 + 16) : (D * 4 + 16);
+  static constexpr int kVBytes = kBf ? D * kVRow : kKeyTile * kVRow;
+  static constexpr int kBytes = kKBytes + kVBytes;
+};
+
+// ---------------------------------------------------------------------------
+// tile loader: global -> registers -> LDS
+// ---------------------------------------------------------------------------
+
+template <typename T, int D, int NT>
+struct TileRegs {
+  static constexpr bool kBf = std::is_same<T, __bf16>::value;
+  // K: 16-byte chunks, D*elt/16 per key.
+  static constexpr int kKChunksPerKey = D * TileCfg<T>::kElt / 16;
+  static constexpr int kKChunks = kKeyTile * kKChunksPerKey;
+  static constexpr int kKPerThread = (kKChunks + NT - 1) / NT;
+  // V (bf16): units of 4 keys x 8 dims; V (fp32): 16-byte chunks like K.
+  static constexpr int kVUnits = kBf ? (kKeyTile / 4) * (D / 8) : kKChunks;
+  static constexpr int kVPerThread = (kVUnits + NT - 1) / NT;
+  static constexpr int kVLoads = kBf ? 4 : 1;
+  u32x4 k[kKPerThread];
+  u32x4 v[kVPerThread][kVLoads];
+
+  __device__ __forceinline__ void load(const unsigned char* kbase, const unsigned char* vbase, int t0, int t1,
+                                       int64_t row_stride_bytes, int tid) {
+#pragma unroll
+    for (int j = 0; j < kKPerThread; ++j) {
+      const int c = tid + j * NT;
+      const int key = c / kKChunksPerKey, ch = c % kKChunksPerKey;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (c < kKChunks && t0 + key < t1)
+        val = *reinterpret_cast<const u32x4*>(kbase + int64_t(t0 + key) * row_stride_bytes + ch * 16);
+      k[j] = val;
+    }
+    if constexpr (kBf) {
+#pragma unroll
+      for (int j = 0; j < kVPerThread; ++j) {
+        const int u = tid + j * NT;
+        const int kg = u / (D / 8), dc = u % (D / 8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u32x4 val = {0u, 0u, 0u, 0u};
+          const int key = 4 * kg + r;
+          if (u < kVUnits && t0 + key < t1)
+            val = *reinterpret_cast<const u32x4*>(vbase + int64_t(t0 + key) * row_stride_bytes + dc * 16);
+          v[j][r] = val;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kVPerThread; ++j) {
+        const int c = tid + j * NT;
+        const int key = c / kKChunksPerKey, ch = c % kKChunksPerKey;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (c < kVUnits && t0 + key < t1)
+          val = *reinterpret_cast<const u32x4*>(vbase + int64_t(t0 + key) * row_stride_bytes + ch * 16);
+        v[j][0] = val;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(unsigned char* lds, int tid) const {
+    using L = Lds<T, D>;
+#pragma unroll
+    for (int j = 0; j < kKPerThread; ++j) {
+      const int c = tid + j * NT;
+      if (c < kKChunks) {
+        const int key = c / kKChunksPerKey, ch = c % kKChunksPerKey;
+        *reinterpret_cast<u32x4*>(lds + key * L::kKRow + ch * 16) = k[j];
+      }
+    }
+    unsigned char* vl = lds + L::kKBytes;
+    if constexpr (kBf) {
+      // 4 keys x 8 dims -> for each dim e, 4 consecutive keys (8 bytes) of Vt[d].
+#pragma unroll
+      for (int j = 0; j < kVPerThread; ++j) {
+        const int u = tid + j * NT;
+        if (u < kVUnits) {
+          const int kg = u / (D / 8), dc = u % (D / 8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int w = e >> 1;
+            const int sh = (e & 1) * 16;
+            const uint32_t k0 = (v[j][0][w] >> sh) & 0xffffu, k1 = (v[j][1][w] >> sh) & 0xffffu;
+            const uint32_t k2 = (v[j][2][w] >> sh) & 0xffffu, k3 = (v[j][3][w] >> sh) & 0xffffu;
+            u32x2 out = {k0 | (k1 << 16), k2 | (k3 << 16)};
+            *reinterpret_cast<u32x2*>(vl + (8 * dc + e) * L::kVRow + kg * 8) = out;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kVPerThread; ++j) {
+        const int c = tid + j * NT;
+        if (c < kVUnits) {
+          const int key = c / kKChunksPerKey, ch = c % kKChunksPerKey;
+          *reinterpret_cast<u32x4*>(vl + key * L::kVRow + ch * 16) = v[j][0];
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// the attention kernel
+// ---------------------------------------------------------------------------
+
+// GH query heads of one KV head per workgroup; 32 / GH tokens per wave; a
+// 64-token row tile therefore takes 2 * GH waves.
+template <typename T, int D, int GH, int MODE>
+__global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
+  constexpr bool kBf = std::is_same<T, __bf16>::value;
+  constexpr int NW = 2 * GH;
+  constexpr int NT = 64 * NW;
+  constexpr int TPW = 32 / GH;
+  constexpr int kQSteps = kBf ? D / 16 : D / 2;  // MFMA k-steps over head_dim
+  constexpr int kDB = D / 32;                    // 32-wide blocks of head_dim
+  using L = Lds<T, D>;
+  using QFrag = typename std::conditional<kBf, bf16x8, float>::type;
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, n = lane & 31;
+  const int kvh = int(blockIdx.x % unsigned(p.hkv));
+  const WorkItem wi = p.work[blockIdx.x / unsigned(p.hkv)];
+  const int tok = wave * TPW + n / GH;
+  const int head = kvh * p.group + int(blockIdx.y) * GH + (n % GH);
+  const bool row_ok = tok < wi.nrows;
+  const int row = wi.row0 + tok;
+
+  int ra = 0, rb = 0;
+  uint64_t rmask = 0;
+  if (row_ok) {
+    ra = p.row_a[row];
+    rb = p.row_b[row];
+    if constexpr (MODE == kVerify) rmask = p.row_mask[row];
+  }
+
+  // Q fragment: lane half h holds dims [(D/2) h, (D/2)(h+1)) of its row.
+  QFrag qf[kQSteps];
+  {
+    const T* qrow = reinterpret_cast<const T*>(p.q) + (int64_t(row) * p.hq + head) * D + (D / 2) * h;
+    if constexpr (kBf) {
+#pragma unroll
+      for (int s = 0; s < kQSteps; ++s) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (row_ok) raw = *reinterpret_cast<const u32x4*>(qrow + 8 * s);
+        qf[s] = __builtin_bit_cast(bf16x8, raw);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < kQSteps; ++s) qf[s] = row_ok ? qrow[s] : 0.f;
+    }
+  }
+
+  f32x16 acc[kDB];
+#pragma unroll
+  for (int md = 0; md < kDB; ++md)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[md][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
+  const int n_b = (wi.b_hi - wi.b_lo + kKeyTile - 1) / kKeyTile;
+  const int n_tiles = n_a + n_b;
+  const int64_t kv_stride = int64_t(p.hkv) * D * TileCfg<T>::kElt;
+  const int64_t head_off = int64_t(kvh) * D * TileCfg<T>::kElt;
+  const unsigned char* ka = reinterpret_cast<const unsigned char*>(p.ka) + head_off;
+  const unsigned char* va = reinterpret_cast<const unsigned char*>(p.va) + head_off;
+  const unsigned char* kb = reinterpret_cast<const unsigned char*>(p.kb) + head_off;
+  const unsigned char* vb = reinterpret_cast<const unsigned char*>(p.vb) + head_off;
+  const int b_full = (wi.flags & kSegBFull) ? wi.b_hi : wi.b_lo;
+
+  TileRegs<T, D, NT> regs;
+  if (n_tiles > 0) {
+    if (n_a > 0)
+      regs.load(ka, va, wi.a_lo, wi.a_hi, kv_stride, tid);
+    else
+      regs.load(kb, vb, wi.b_lo, wi.b_hi, kv_stride, tid);
+  }
+
+  const unsigned char* kl = lds;
+  const unsigned char* vl = lds + L::kKBytes;
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const bool seg_a = it < n_a;
+    const int t0 = seg_a ? wi.a_lo + it * kKeyTile : wi.b_lo + (it - n_a) * kKeyTile;
+    const int t_hi = seg_a ? wi.a_hi : wi.b_hi;
+    const int t_full = seg_a ? wi.a_full : b_full;
+
+    __syncthreads();
+    regs.store(lds, tid);
+    __syncthreads();
+    if (it + 1 < n_tiles) {
+      const int nx = it + 1;
+      if (nx < n_a)
+        regs.load(ka, va, wi.a_lo + nx * kKeyTile, wi.a_hi, kv_stride, tid);
+      else
+        regs.load(kb, vb, wi.b_lo + (nx - n_a) * kKeyTile, wi.b_hi, kv_stride, tid);
+    }
+    // waves without any valid row skip the math (the tile is still staged)
+    if (wave * TPW >= wi.nrows) continue;
+
+    // ---- S^T = K Q^T for two 32-key blocks ----
+    f32x16 s[2];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[bk][i] = 0.f;
+      const int krow = 32 * bk + key_perm(n);
+      if constexpr (kBf) {
+#pragma unroll
+        for (int st = 0; st < kQSteps; ++st) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + krow * L::kKRow + (D * h + 16 * st));
+          s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[bk], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < kQSteps; ++st) {
+          const float a = *reinterpret_cast<const float*>(kl + krow * L::kKRow + ((D / 2) * h + st) * 4);
+          s[bk] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[st], s[bk], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- visibility (only tiles that reach past the all-visible prefix) ----
+    if (t0 + kKeyTile > t_full) {
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = t0 + 32 * bk + reg_key(i, h);
+          bool vis = key < t_hi;
+          if (row_ok) {
+            if (seg_a) {
+              if constexpr (MODE != kVerify) vis = vis && key < ra;
+            } else {
+              if constexpr (MODE == kPrefill) {
+                vis = vis && key >= rb && key <= row;
+              } else if constexpr (MODE == kVerify) {
+                const unsigned rel = unsigned(key - rb);
+                vis = vis && rel < 64u && ((rmask >> (rel & 63u)) & 1ull);
+              }
+            }
+          }
+          s[bk][i] = vis ? s[bk][i] : -INFINITY;
+        }
+      }
+    }
+
+    // ---- online softmax ----
+    float mt = s[0][0];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[bk][i]);
+    mt = fmaxf(mt, shfl_xor32(mt));
+    const float m_new = fmaxf(m_run, mt);
+    if (__any(m_new > m_run)) {
+      const float alpha = (m_new > m_run) ? fast_exp2((m_run - m_new) * p.c) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < kDB; ++md)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[md][i] *= alpha;
+    }
+    m_run = m_new;
+    const float mb = (m_new == -INFINITY) ? 0.f : m_new * p.c;
+    float ls = 0.f;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(fmaf(s[bk][i], p.c, -mb));
+        s[bk][i] = e;
+        ls += e;
+      }
+    l_run += ls;
+
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+      if constexpr (kBf) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          u32x4 pw;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(s[bk][8 * c2 + 2 * j], s[bk][8 * c2 + 2 * j + 1]);
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+          const int kcol = (32 * bk + 16 * c2 + 8 * h) * 2;
+#pragma unroll
+          for (int md = 0; md < kDB; ++md) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(vl + (32 * md + n) * L::kVRow + kcol);
+            acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[md], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = 32 * bk + reg_key(i, h);
+#pragma unroll
+          for (int md = 0; md < kDB; ++md) {
+            const float a = *reinterpret_cast<const float*>(vl + key * L::kVRow + (32 * md + n) * 4);
+            acc[md] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[bk][i], acc[md], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- epilogue ----
+  const float l_tot = l_run + shfl_xor32(l_run);
+  if (!row_ok) return;
+  if constexpr (MODE == kDecode) {
+    const int64_t slot = int64_t(wi.out) + tok;
+    const int64_t idx = slot * p.hq + head;
+    float* dst = p.part_acc + idx * D;
+#pragma unroll
+    for (int md = 0; md < kDB; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * md + 8 * g + 4 * h;
+        float4 vv = {acc[md][4 * g], acc[md][4 * g + 1], acc[md][4 * g + 2], acc[md][4 * g + 3]};
+        *reinterpret_cast<float4*>(dst + d0) = vv;
+      }
+    if (h == 0) {
+      float2 ml = {m_run == -INFINITY ? -INFINITY : m_run * p.c, l_tot};
+      *reinterpret_cast<float2*>(p.part_ml + idx * 2) = ml;
+    }
+  } else {
+    const float inv = 1.f / l_tot;
+    T* dst = reinterpret_cast<T*>(p.o) + (int64_t(row) * p.hq + head) * D;
+#pragma unroll
+    for (int md = 0; md < kDB; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * md + 8 * g + 4 * h;
+        if constexpr (kBf) {
+          u32x2 w = {pack_bf16x2(acc[md][4 * g] * inv, acc[md][4 * g + 1] * inv),
+                     pack_bf16x2(acc[md][4 * g + 2] * inv, acc[md][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(dst + d0) = w;
+        } else {
+          float4 vv = {acc[md][4 * g] * inv, acc[md][4 * g + 1] * inv, acc[md][4 * g + 2] * inv,
+                       acc[md][4 * g + 3] * inv};
+          *reinterpret_cast<float4*>(dst + d0) = vv;
+        }
+      }
+    if (p.lse && h == 0) p.lse[int64_t(head) * p.n_rows + row] = (m_run * p.c + __log2f(l_tot)) * 0.69314718055994531f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode merge: one (branch, query head) per 64-lane group, fixed order
+// ---------------------------------------------------------------------------
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  constexpr int kPer = D / 64 > 0 ? D / 64 : 1;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (pair >= int64_t(p.n_rows) * p.hq) return;
+  const int row = int(pair / p.hq), head = int(pair % p.hq);
+  const MergeRow mr = p.merge[row];
+  float mx = -INFINITY;
+  for (int c = 0; c < mr.sh_count; ++c)
+    mx = fmaxf(mx, p.part_ml[(int64_t(mr.sh_first + c * mr.sh_stride) * p.hq + head) * 2]);
+  for (int c = 0; c < mr.sf_count; ++c) mx = fmaxf(mx, p.part_ml[(int64_t(mr.sf_first + c) * p.hq + head) * 2]);
+  float acc[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) acc[j] = 0.f;
+  float l = 0.f;
+  const int n_parts = mr.sh_count + mr.sf_count;
+  for (int c = 0; c < n_parts; ++c) {
+    const int64_t slot = c < mr.sh_count ? int64_t(mr.sh_first) + int64_t(c) * mr.sh_stride
+                                         : int64_t(mr.sf_first) + (c - mr.sh_count);
+    const int64_t idx = slot * p.hq + head;
+    const float m = p.part_ml[idx * 2];
+    const float w = (m == -INFINITY) ? 0.f : fast_exp2(m - mx);
+    l += w * p.part_ml[idx * 2 + 1];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int d = lane + 64 * j;
+      if (d < D) acc[j] += w * p.part_acc[idx * D + d];
+    }
+  }
+  const float inv = 1.f / l;
+  T* dst = reinterpret_cast<T*>(p.o) + (int64_t(row) * p.hq + head) * D;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int d = lane + 64 * j;
+    if (d < D) dst[d] = static_cast<T>(acc[j] * inv);
+  }
+  if (p.lse && lane == 0) p.lse[int64_t(head) * p.n_rows + row] = (mx + __log2f(l)) * 0.69314718055994531f;
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+template <typename T, int D, int GH, int MODE>
+static hipError_t launch_t(const AttnParams& p, int n_work, hipStream_t st) {
+  dim3 grid(unsigned(n_work) * unsigned(p.hkv), unsigned(p.group / GH));
+  hipLaunchKernelGGL((attn_kernel<T, D, GH, MODE>), grid, dim3(128 * GH), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename T, int MODE>
+static hipError_t launch_d(const AttnParams& p, int n_work, int d, hipStream_t st) {
+  const int gh = p.group == 1 ? 1 : 2;
+  switch (d * 4 + gh) {
+    case 32 * 4 + 1: return launch_t<T, 32, 1, MODE>(p, n_work, st);
+    case 32 * 4 + 2: return launch_t<T, 32, 2, MODE>(p, n_work, st);
+    case 64 * 4 + 1: return launch_t<T, 64, 1, MODE>(p, n_work, st);
+    case 64 * 4 + 2: return launch_t<T, 64, 2, MODE>(p, n_work, st);
+    case 128 * 4 + 1: return launch_t<T, 128, 1, MODE>(p, n_work, st);
+    case 128 * 4 + 2: return launch_t<T, 128, 2, MODE>(p, n_work, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attention(int mode, int dtype, const AttnParams& p, int n_work, int d, hipStream_t st) {
+  if (n_work == 0) return hipSuccess;
+  if (dtype == TA_DTYPE_BF16) {
+    if (mode == kPrefill) return launch_d<__bf16, kPrefill>(p, n_work, d, st);
+    if (mode == kVerify) return launch_d<__bf16, kVerify>(p, n_work, d, st);
+    return launch_d<__bf16, kDecode>(p, n_work, d, st);
+  }
+  if (mode == kPrefill) return launch_d<float, kPrefill>(p, n_work, d, st);
+  if (mode == kVerify) return launch_d<float, kVerify>(p, n_work, d, st);
+  return launch_d<float, kDecode>(p, n_work, d, st);
+}
+
+hipError_t launch_merge(int dtype, const MergeParams& p, int d, hipStream_t st) {
+  const int64_t pairs = int64_t(p.n_rows) * p.hq;
+  if (pairs == 0) return hipSuccess;
+  dim3 grid(unsigned((pairs + 3) / 4));
+  if (dtype == TA_DTYPE_BF16) {
+    if (d == 32) hipLaunchKernelGGL((merge_kernel<__bf16, 32>), grid, dim3(256), 0, st, p);
+    else if (d == 64) hipLaunchKernelGGL((merge_kernel<__bf16, 64>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((merge_kernel<__bf16, 128>), grid, dim3(256), 0, st, p);
+  } else {
+    if (d == 32) hipLaunchKernelGGL((merge_kernel<float, 32>), grid, dim3(256), 0, st, p);
+    else if (d == 64) hipLaunchKernelGGL((merge_kernel<float, 64>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((merge_kernel<float, 128>), grid, dim3(256), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ta

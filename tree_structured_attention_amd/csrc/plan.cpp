@@ -1,0 +1,404 @@
+// Host plan builder: turns a page/branch/tree description into per-row key
+// bounds, tree bitmasks and an ordered work list.  Integer work only; no GPU.
+//
+// Visibility it encodes (sources named in the public header):
+//   prefill  row in the main stream of a page: keys [page_base, row]
+//            row Y_k[t]: keys [page_base, page_base + P + L_<=k) and
+//            [start of Y_k, row]   (ancestor sets of the PaDoc summary,
+//            "Training paradigm")
+//   decode   branch (page p, region k, s_k): main_p[0, P + L_<=k) plus its
+//            own s_k + 1 suffix tokens (PaDoc summary, "Inference")
+//   verify   node i: its page's context plus anc*(i) inside its tree (HSD
+//            notes, key design 3 (b))
+// With the packed order [X | B_1..B_N | Y_1..Y_N] a row's visible keys are
+// at most two contiguous intervals, so no mask memory is needed outside the
+// 64-node draft trees.
+#include <algorithm>
+#include <climits>
+#include <cstring>
+#include <numeric>
+
+#include "ta_internal.h"
+
+namespace ta {
+
+namespace {
+
+constexpr int64_t kMax32 = INT32_MAX;
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+int64_t item_cost(const WorkItem& w) {
+  return int64_t(w.nrows) * (int64_t(w.a_hi - w.a_lo) + int64_t(w.b_hi - w.b_lo) + 16);
+}
+
+// Longest first, so that the long tiles start early and the short ones fill
+// the tail; ties keep plan order.
+void order_work(std::vector<WorkItem>& w) {
+  std::stable_sort(w.begin(), w.end(),
+                   [](const WorkItem& x, const WorkItem& y) { return item_cost(x) > item_cost(y); });
+}
+
+WorkItem make_item(int64_t row0, int64_t nrows, int64_t a_lo, int64_t a_full, int64_t a_hi,
+                   int64_t b_lo, int64_t b_hi, int64_t out, int32_t flags) {
+  WorkItem w{};
+  w.row0 = int32_t(row0);
+  w.nrows = int32_t(nrows);
+  w.a_lo = int32_t(a_lo);
+  w.a_full = int32_t(std::max(a_lo, std::min(a_full, a_hi)));
+  w.a_hi = int32_t(a_hi);
+  w.b_lo = int32_t(b_lo);
+  w.b_hi = int32_t(std::max(b_lo, b_hi));
+  w.out = int32_t(out);
+  w.flags = flags;
+  return w;
+}
+
+}  // namespace
+
+void pack_blob(ta_plan* p) {
+  DeviceLayout L;
+  int64_t off = 0;
+  L.work = off;
+  off = align256(off + int64_t(p->work.size() * sizeof(WorkItem)));
+  L.row_a = off;
+  off = align256(off + int64_t(p->row_a.size() * 4));
+  L.row_b = off;
+  off = align256(off + int64_t(p->row_b.size() * 4));
+  L.mask = off;
+  off = align256(off + int64_t(p->row_mask.size() * 8));
+  L.merge = off;
+  off = align256(off + int64_t(p->merge.size() * sizeof(MergeRow)));
+  L.total = std::max<int64_t>(off, 256);
+  p->layout = L;
+  p->blob.assign(size_t(L.total), 0);
+  auto put = [&](int64_t at, const void* src, size_t n) {
+    if (n) std::memcpy(p->blob.data() + at, src, n);
+  };
+  put(L.work, p->work.data(), p->work.size() * sizeof(WorkItem));
+  put(L.row_a, p->row_a.data(), p->row_a.size() * 4);
+  put(L.row_b, p->row_b.data(), p->row_b.size() * 4);
+  put(L.mask, p->row_mask.data(), p->row_mask.size() * 8);
+  put(L.merge, p->merge.data(), p->merge.size() * sizeof(MergeRow));
+}
+
+}  // namespace ta
+
+using namespace ta;
+
+extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* n_regions,
+                                      const int32_t* layout_len, const int32_t* content_len,
+                                      int32_t n_pages, ta_plan** out) {
+  if (!out) return fail(TA_ERR_INVALID_ARG, "plan_prefill: out is NULL");
+  if (n_pages < 0) return fail(TA_ERR_INVALID_ARG, "plan_prefill: n_pages < 0");
+  if (n_pages > 0 && (!prefix_len || !n_regions))
+    return fail(TA_ERR_INVALID_ARG, "plan_prefill: NULL prefix_len/n_regions");
+  int64_t total_regions = 0, total_tokens = 0;
+  for (int32_t p = 0; p < n_pages; ++p) {
+    if (prefix_len[p] < 0) return fail(TA_ERR_INVALID_ARG, "plan_prefill: negative prefix_len");
+    if (n_regions[p] < 0) return fail(TA_ERR_INVALID_ARG, "plan_prefill: negative n_regions");
+    total_regions += n_regions[p];
+  }
+  if (total_regions > 0 && (!layout_len || !content_len))
+    return fail(TA_ERR_INVALID_ARG, "plan_prefill: NULL layout_len/content_len");
+  for (int64_t r = 0; r < total_regions; ++r) {
+    if (layout_len[r] < 0 || content_len[r] < 0)
+      return fail(TA_ERR_INVALID_ARG, "plan_prefill: negative layout/content length");
+  }
+  {
+    int64_t r = 0;
+    for (int32_t p = 0; p < n_pages; ++p) {
+      total_tokens += prefix_len[p];
+      for (int32_t k = 0; k < n_regions[p]; ++k, ++r) total_tokens += int64_t(layout_len[r]) + content_len[r];
+      if (total_tokens >= kMax32) return fail(TA_ERR_CAPACITY, "plan_prefill: packed length >= 2^31");
+    }
+  }
+
+  auto* pl = new ta_plan();
+  pl->kind = TA_PLAN_PREFILL;
+  pl->n_pages = n_pages;
+  pl->n_branches = int32_t(total_regions);
+  pl->n_rows = total_tokens;
+  pl->n_keys_a = pl->n_keys_b = total_tokens;
+  pl->row_a.resize(size_t(total_tokens));
+  pl->row_b.resize(size_t(total_tokens));
+  pl->position.resize(size_t(total_tokens));
+  pl->main_end.resize(size_t(total_tokens));
+  pl->branch_start.resize(size_t(total_tokens));
+
+  int64_t base = 0, r = 0;
+  for (int32_t p = 0; p < n_pages; ++p) {
+    const int64_t P = prefix_len[p];
+    const int32_t N = n_regions[p];
+    int64_t sumL = 0, sumC = 0;
+    for (int32_t k = 0; k < N; ++k) {
+      sumL += layout_len[r + k];
+      sumC += content_len[r + k];
+    }
+    const int64_t M = P + sumL, T = M + sumC;
+    // main stream: causal over [X | B]
+    for (int64_t i = 0; i < M; ++i) {
+      const int64_t row = base + i;
+      pl->position[row] = i;
+      pl->main_end[row] = row + 1;
+      pl->branch_start[row] = row + 1;
+    }
+    // branches
+    int64_t accL = 0, accC = 0, depth = 0;
+    for (int32_t k = 0; k < N; ++k) {
+      accL += layout_len[r + k];
+      const int64_t ck = content_len[r + k];
+      const int64_t b0 = base + M + accC;
+      const int64_t bound = base + P + accL;
+      pl->branches3.insert(pl->branches3.end(), {bound, b0, ck});
+      for (int64_t t = 0; t < ck; ++t) {
+        pl->position[b0 + t] = P + accL + t;
+        pl->main_end[b0 + t] = bound;
+        pl->branch_start[b0 + t] = b0;
+      }
+      accC += ck;
+      depth = std::max(depth, accL + ck);
+    }
+    pl->pages5.insert(pl->pages5.end(), {base, M, T, depth, sumL + sumC});
+    pl->max_depth = std::max(pl->max_depth, depth);
+    for (int64_t i = 0; i < T; ++i) pl->visible_pairs += pl->position[base + i] + 1;
+
+    // row tiles of this page
+    for (int64_t t0 = 0; t0 < T; t0 += kTileTokens) {
+      const int64_t t1 = std::min(T, t0 + kTileTokens);
+      int64_t a_hi = base, a_full = INT64_MAX, b_lo = INT64_MAX, b_hi = 0;
+      bool any_branch = false;
+      for (int64_t i = base + t0; i < base + t1; ++i) {
+        a_hi = std::max(a_hi, pl->main_end[i]);
+        a_full = std::min(a_full, pl->main_end[i]);
+        if (pl->branch_start[i] <= i) {
+          any_branch = true;
+          b_lo = std::min(b_lo, pl->branch_start[i]);
+          b_hi = std::max(b_hi, i + 1);
+        }
+      }
+      if (!any_branch) b_lo = b_hi = 0;
+      // a main-stream row's own causal bound is inside segment A, so a tile
+      // holding main rows is fully visible only below its first row.
+      pl->work.push_back(make_item(base + t0, t1 - t0, base, a_full, a_hi, b_lo, b_hi, -1, 0));
+    }
+    base += T;
+    r += N;
+  }
+  for (int64_t i = 0; i < total_tokens; ++i) {
+    pl->row_a[i] = int32_t(pl->main_end[i]);
+    pl->row_b[i] = int32_t(pl->branch_start[i]);
+  }
+  order_work(pl->work);
+  pack_blob(pl);
+  *out = pl;
+  return TA_OK;
+}
+
+extern "C" int tree_attn_plan_decode(const int32_t* prefix_len, const int32_t* n_regions,
+                                     const int32_t* layout_len, int32_t n_pages,
+                                     const int32_t* br_page, const int32_t* br_region,
+                                     const int32_t* suffix_len, int32_t n_branches,
+                                     ta_plan** out) {
+  if (!out) return fail(TA_ERR_INVALID_ARG, "plan_decode: out is NULL");
+  if (n_pages < 0 || n_branches < 0) return fail(TA_ERR_INVALID_ARG, "plan_decode: negative count");
+  if (n_pages > 0 && (!prefix_len || !n_regions))
+    return fail(TA_ERR_INVALID_ARG, "plan_decode: NULL prefix_len/n_regions");
+  if (n_branches > 0 && (!br_page || !br_region || !suffix_len))
+    return fail(TA_ERR_INVALID_ARG, "plan_decode: NULL branch arrays");
+  std::vector<int64_t> reg_off(size_t(n_pages) + 1, 0), main_off(size_t(n_pages) + 1, 0);
+  for (int32_t p = 0; p < n_pages; ++p) {
+    if (prefix_len[p] < 0 || n_regions[p] < 0) return fail(TA_ERR_INVALID_ARG, "plan_decode: negative page size");
+    reg_off[p + 1] = reg_off[p] + n_regions[p];
+  }
+  if (reg_off[n_pages] > 0 && !layout_len) return fail(TA_ERR_INVALID_ARG, "plan_decode: NULL layout_len");
+  for (int32_t p = 0; p < n_pages; ++p) {
+    int64_t m = prefix_len[p];
+    for (int64_t r = reg_off[p]; r < reg_off[p + 1]; ++r) {
+      if (layout_len[r] < 0) return fail(TA_ERR_INVALID_ARG, "plan_decode: negative layout_len");
+      m += layout_len[r];
+    }
+    main_off[p + 1] = main_off[p] + m;
+    if (main_off[p + 1] >= kMax32) return fail(TA_ERR_CAPACITY, "plan_decode: main tokens >= 2^31");
+  }
+  int64_t suffix_total = 0;
+  for (int32_t b = 0; b < n_branches; ++b) {
+    if (br_page[b] < 0 || br_page[b] >= n_pages) return fail(TA_ERR_INVALID_ARG, "plan_decode: br_page out of range");
+    if (b > 0 && br_page[b] < br_page[b - 1])
+      return fail(TA_ERR_INVALID_ARG, "plan_decode: branches must be grouped by page (br_page non-decreasing)");
+    if (br_region[b] < 1 || br_region[b] > n_regions[br_page[b]])
+      return fail(TA_ERR_INVALID_ARG, "plan_decode: br_region must be in 1..N of its page");
+    if (suffix_len[b] < 0) return fail(TA_ERR_INVALID_ARG, "plan_decode: negative suffix_len");
+    suffix_total += int64_t(suffix_len[b]) + 1;
+    if (suffix_total >= kMax32) return fail(TA_ERR_CAPACITY, "plan_decode: suffix tokens >= 2^31");
+  }
+
+  auto* pl = new ta_plan();
+  pl->kind = TA_PLAN_DECODE;
+  pl->n_pages = n_pages;
+  pl->n_branches = n_branches;
+  pl->n_rows = n_branches;
+  pl->n_keys_a = main_off[n_pages];
+  pl->n_keys_b = suffix_total;
+  pl->row_a.resize(size_t(n_branches));
+  pl->row_b.assign(size_t(n_branches), 0);
+  pl->merge.resize(size_t(n_branches));
+
+  std::vector<int64_t> main_len(static_cast<size_t>(n_branches)), suf_start(static_cast<size_t>(n_branches));
+  int64_t s0 = 0;
+  for (int32_t b = 0; b < n_branches; ++b) {
+    const int32_t p = br_page[b];
+    int64_t m = prefix_len[p];
+    for (int32_t k = 0; k < br_region[b]; ++k) m += layout_len[reg_off[p] + k];
+    main_len[b] = m;
+    suf_start[b] = s0;
+    pl->row_a[b] = int32_t(main_off[p] + m);
+    pl->decode_rows5.insert(pl->decode_rows5.end(),
+                            {main_off[p], m, s0, int64_t(suffix_len[b]) + 1, m + suffix_len[b]});
+    pl->visible_pairs += m + suffix_len[b] + 1;
+    s0 += int64_t(suffix_len[b]) + 1;
+  }
+
+  // Pass-1 work items.  Partial slots (per query head) are numbered in plan
+  // order: a shared chunk owns one slot per branch of its row group, a
+  // suffix chunk one slot.
+  int64_t slot = 0;
+  int32_t b = 0;
+  while (b < n_branches) {
+    const int32_t p = br_page[b];
+    int32_t e = b;
+    while (e < n_branches && br_page[e] == p) ++e;
+    // row groups of at most one tile of branches
+    for (int32_t g0 = b; g0 < e; g0 += kTileTokens) {
+      const int32_t g1 = std::min(e, g0 + kTileTokens);
+      int64_t hi = 0, lo_bound = INT64_MAX;
+      for (int32_t i = g0; i < g1; ++i) {
+        hi = std::max(hi, main_len[i]);
+        lo_bound = std::min(lo_bound, main_len[i]);
+      }
+      const int64_t n_chunks = (hi + kDecodeChunk - 1) / kDecodeChunk;
+      const int64_t first = slot;
+      for (int64_t c = 0; c < n_chunks; ++c) {
+        const int64_t c0 = c * kDecodeChunk, c1 = std::min(hi, c0 + kDecodeChunk);
+        pl->work.push_back(make_item(g0, g1 - g0, main_off[p] + c0, main_off[p] + lo_bound, main_off[p] + c1,
+                                     0, 0, slot, 0));
+        slot += g1 - g0;
+      }
+      for (int32_t i = g0; i < g1; ++i) {
+        MergeRow& mr = pl->merge[i];
+        mr.sh_first = int32_t(first + (i - g0));
+        mr.sh_count = int32_t((main_len[i] + kDecodeChunk - 1) / kDecodeChunk);
+        mr.sh_stride = g1 - g0;
+      }
+    }
+    b = e;
+  }
+  for (int32_t i = 0; i < n_branches; ++i) {
+    const int64_t len = int64_t(suffix_len[i]) + 1;
+    const int64_t chunk = len <= kDecodeSuffixWhole ? len : kDecodeChunk;
+    const int64_t n_chunks = (len + chunk - 1) / chunk;
+    pl->merge[i].sf_first = int32_t(slot);
+    pl->merge[i].sf_count = int32_t(n_chunks);
+    for (int64_t c = 0; c < n_chunks; ++c) {
+      const int64_t c0 = suf_start[i] + c * chunk, c1 = std::min(suf_start[i] + len, c0 + chunk);
+      pl->work.push_back(make_item(i, 1, 0, 0, 0, c0, c1, slot, kSegBFull));
+      slot += 1;
+    }
+  }
+  if (slot >= kMax32) {
+    delete pl;
+    return fail(TA_ERR_CAPACITY, "plan_decode: partial slots >= 2^31");
+  }
+  pl->n_partials = slot;
+  order_work(pl->work);
+  pack_blob(pl);
+  *out = pl;
+  return TA_OK;
+}
+
+extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page,
+                                     const int32_t* n_nodes, const int32_t* parent, int32_t n_branches,
+                                     ta_plan** out) {
+  if (!out) return fail(TA_ERR_INVALID_ARG, "plan_verify: out is NULL");
+  if (n_pages < 0 || n_branches < 0) return fail(TA_ERR_INVALID_ARG, "plan_verify: negative count");
+  if (n_pages > 0 && !ctx_len) return fail(TA_ERR_INVALID_ARG, "plan_verify: NULL ctx_len");
+  if (n_branches > 0 && (!br_page || !n_nodes)) return fail(TA_ERR_INVALID_ARG, "plan_verify: NULL branch arrays");
+  std::vector<int64_t> ctx_off(size_t(n_pages) + 1, 0);
+  for (int32_t p = 0; p < n_pages; ++p) {
+    if (ctx_len[p] < 0) return fail(TA_ERR_INVALID_ARG, "plan_verify: negative ctx_len");
+    ctx_off[p + 1] = ctx_off[p] + ctx_len[p];
+    if (ctx_off[p + 1] >= kMax32) return fail(TA_ERR_CAPACITY, "plan_verify: context tokens >= 2^31");
+  }
+  int64_t total_nodes = 0;
+  for (int32_t b = 0; b < n_branches; ++b) {
+    if (br_page[b] < 0 || br_page[b] >= n_pages) return fail(TA_ERR_INVALID_ARG, "plan_verify: br_page out of range");
+    if (b > 0 && br_page[b] < br_page[b - 1])
+      return fail(TA_ERR_INVALID_ARG, "plan_verify: trees must be grouped by page (br_page non-decreasing)");
+    if (n_nodes[b] < 0) return fail(TA_ERR_INVALID_ARG, "plan_verify: negative n_nodes");
+    if (n_nodes[b] > 64) return fail(TA_ERR_CAPACITY, "plan_verify: a tree has more than 64 nodes");
+    total_nodes += n_nodes[b];
+    if (total_nodes >= kMax32) return fail(TA_ERR_CAPACITY, "plan_verify: nodes >= 2^31");
+  }
+  if (total_nodes > 0 && !parent) return fail(TA_ERR_INVALID_ARG, "plan_verify: NULL parent");
+  {
+    int64_t off = 0;
+    for (int32_t b = 0; b < n_branches; ++b) {
+      for (int32_t i = 0; i < n_nodes[b]; ++i) {
+        const int32_t pa = parent[off + i];
+        if (pa < -1 || pa >= i)
+          return fail(TA_ERR_INVALID_ARG, "plan_verify: parent must be -1 or an earlier node of the same tree");
+      }
+      off += n_nodes[b];
+    }
+  }
+
+  auto* pl = new ta_plan();
+  pl->kind = TA_PLAN_VERIFY;
+  pl->n_pages = n_pages;
+  pl->n_branches = n_branches;
+  pl->n_rows = total_nodes;
+  pl->n_keys_a = ctx_off[n_pages];
+  pl->n_keys_b = total_nodes;
+  pl->row_a.resize(size_t(total_nodes));
+  pl->row_b.resize(size_t(total_nodes));
+  pl->row_mask.resize(size_t(total_nodes));
+  pl->verify_mask.resize(size_t(total_nodes));
+
+  std::vector<int64_t> node_off(size_t(n_branches) + 1, 0);
+  for (int32_t b = 0; b < n_branches; ++b) node_off[b + 1] = node_off[b] + n_nodes[b];
+  for (int32_t b = 0; b < n_branches; ++b) {
+    const int32_t p = br_page[b];
+    std::vector<uint64_t> bits(static_cast<size_t>(n_nodes[b]));
+    std::vector<int64_t> dep(static_cast<size_t>(n_nodes[b]));
+    for (int32_t i = 0; i < n_nodes[b]; ++i) {
+      const int32_t pa = parent[node_off[b] + i];
+      bits[i] = (pa < 0 ? 0ull : bits[pa]) | (1ull << i);
+      dep[i] = pa < 0 ? 0 : dep[pa] + 1;
+      const int64_t row = node_off[b] + i;
+      pl->row_a[row] = int32_t(ctx_off[p + 1]);
+      pl->row_b[row] = int32_t(node_off[b]);
+      pl->row_mask[row] = bits[i];
+      pl->verify_mask[row] = int64_t(bits[i]);
+      pl->verify_rows4.insert(pl->verify_rows4.end(), {ctx_off[p], int64_t(ctx_len[p]), node_off[b], ctx_len[p] + dep[i]});
+      pl->visible_pairs += ctx_len[p] + dep[i] + 1;
+      pl->max_depth = std::max(pl->max_depth, dep[i]);
+    }
+  }
+  // Row tiles: whole trees of one page, at most one tile of nodes.
+  int32_t b = 0;
+  while (b < n_branches) {
+    const int32_t p = br_page[b];
+    int32_t e = b;
+    int64_t nodes = 0;
+    while (e < n_branches && br_page[e] == p && nodes + n_nodes[e] <= kTileTokens) nodes += n_nodes[e++];
+    if (nodes > 0) {
+      pl->work.push_back(make_item(node_off[b], nodes, ctx_off[p], ctx_off[p + 1], ctx_off[p + 1],
+                                   node_off[b], node_off[e], -1, 0));
+    }
+    b = e;
+  }
+  order_work(pl->work);
+  pack_blob(pl);
+  *out = pl;
+  return TA_OK;
+}

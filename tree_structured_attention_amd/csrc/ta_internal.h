@@ -1,0 +1,84 @@
+// Internal definitions shared by the plan builder, the C ABI and the kernel
+// launchers of libtree_attn.  Not part of the public interface.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/tree_attn.h"
+
+namespace ta {
+
+// Every launch walks row tiles of this many query tokens.
+constexpr int kTileTokens = 64;
+// Keys per LDS tile.
+constexpr int kKeyTile = 64;
+// Decode splits a page's main stream (and long suffixes) into chunks of
+// this many keys; each chunk is one work item producing fp32 partials.
+constexpr int kDecodeChunk = 1024;
+// Suffixes up to this length stay in one work item.
+constexpr int kDecodeSuffixWhole = 2048;
+
+// One work item: a tile of query rows and the two key segments it walks.
+//   rows  [row0, row0 + nrows)
+//   seg A [a_lo, a_hi): keys [a_lo, a_full) are visible to every row of the
+//         tile; keys in [a_full, a_hi) are tested per row against row_a.
+//   seg B [b_lo, b_hi): always tested per row (prefill: branch-causal;
+//         verify: tree bitmask; decode suffix: visible, flag kSegBFull).
+//   out   decode: first partial slot of the tile (per query head); else -1.
+//   flags bit 0: seg B fully visible.
+struct WorkItem {
+  int32_t row0, nrows, a_lo, a_full, a_hi, b_lo, b_hi, out;
+  int32_t flags, pad0, pad1, pad2;
+};
+static_assert(sizeof(WorkItem) == 48, "work item layout");
+constexpr int32_t kSegBFull = 1;
+
+// Decode merge table, one entry per live branch: shared partial slots are
+// sh_first + c * sh_stride (c < sh_count), suffix slots sf_first + c.
+struct MergeRow {
+  int32_t sh_first, sh_count, sh_stride, sf_first, sf_count, pad0, pad1, pad2;
+};
+static_assert(sizeof(MergeRow) == 32, "merge row layout");
+
+// Offsets (bytes) of the tables inside the device workspace.
+struct DeviceLayout {
+  int64_t work = 0, row_a = 0, row_b = 0, mask = 0, merge = 0, total = 0;
+};
+
+}  // namespace ta
+
+struct ta_plan {
+  int32_t kind = 0;
+  int32_t n_pages = 0;
+  int32_t n_branches = 0;
+  int64_t n_rows = 0;
+  int64_t n_keys_a = 0;
+  int64_t n_keys_b = 0;
+  int64_t n_partials = 0;
+  int64_t visible_pairs = 0;
+  int64_t max_depth = 0;
+
+  // device tables (host copies)
+  std::vector<ta::WorkItem> work;
+  std::vector<int32_t> row_a, row_b;
+  std::vector<uint64_t> row_mask;
+  std::vector<ta::MergeRow> merge;
+  ta::DeviceLayout layout;
+  std::vector<unsigned char> blob;  // packed image of the device tables
+
+  // exported semantic fields
+  std::vector<int64_t> position, main_end, branch_start, pages5, branches3;
+  std::vector<int64_t> decode_rows5, verify_rows4, verify_mask;
+
+  // binding to device memory
+  void* dev = nullptr;
+  void* upload_event = nullptr;  // hipEvent_t of the last upload
+};
+
+namespace ta {
+void set_error(const std::string& msg);
+int fail(int code, const std::string& msg);
+void pack_blob(ta_plan* p);
+}  // namespace ta

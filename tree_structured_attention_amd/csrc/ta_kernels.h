@@ -1,0 +1,45 @@
+// Kernel launch interface between the C ABI layer and attn_kernels.hip.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "ta_internal.h"
+
+namespace ta {
+
+enum Mode : int { kPrefill = 0, kVerify = 1, kDecode = 2 };
+
+struct AttnParams {
+  const void* q;
+  const void* ka;
+  const void* va;
+  const void* kb;
+  const void* vb;
+  void* o;
+  float* lse;
+  float* part_acc;  // decode: [n_partials, hq, d] unnormalised fp32 accumulators
+  float* part_ml;   // decode: [n_partials, hq, 2] (running max in log2 units of the scaled score, sum)
+  const WorkItem* work;
+  const int32_t* row_a;
+  const int32_t* row_b;
+  const uint64_t* row_mask;
+  int32_t hq, hkv, group;
+  float c;  // softmax scale * log2(e)
+  int64_t n_rows;
+};
+
+struct MergeParams {
+  const MergeRow* merge;
+  const float* part_acc;
+  const float* part_ml;
+  void* o;
+  float* lse;
+  int32_t n_rows, hq;
+};
+
+hipError_t launch_attention(int mode, int dtype, const AttnParams& p, int n_work, int head_dim, hipStream_t st);
+hipError_t launch_merge(int dtype, const MergeParams& p, int head_dim, hipStream_t st);
+
+}  // namespace ta
