@@ -1,0 +1,269 @@
+"""Benchmark of the tree attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of every entry point over resident synthetic inputs:
+  prefill  one packed page: P = 4096, 24 regions of 12 layout tokens,
+           lognormal content (8,772 tokens), 16q/8kv heads, d = 128, bf16
+  decode   16 pages x 24 live branches, P = 4809, s_k ~ U{0..1024}
+  verify   64 pages x 8 draft trees of 32 nodes, contexts ~ U{4096..16384}
+Each entry point is bracketed by HIP events on the stream it is launched on
+(torch's current stream).  The single JSON line on stdout reports prefill
+packed tokens/s as `value`, with decode and verify beside it, a roofline per
+kernel (algorithmic FLOPs or bytes per launch over the measured average
+launch time) and the fp64 CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from tree_structured_attention_amd import binding as ta  # noqa: E402
+from tree_structured_attention_amd import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "tree-attn prefill tokens/s + %MFMA peak; branch-decode tokens/s + %HBM BW"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def elt(dtype):
+    return 2 if dtype == torch.bfloat16 else 4
+
+
+def prefill_case():
+    w = synth.config2()
+    t0 = time.perf_counter()
+    plan = ta.plan_for(w.desc)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    plan.upload()
+    t = {k: v.cuda() for k, v in w.tensors.items()}
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((w.hq, t["q"].shape[0]), dtype=torch.float32, device="cuda")
+    info = plan.info
+
+    def run():
+        ta.prefill(plan, t["q"], t["k"], t["v"], scale=w.scale, out=o, lse=lse)
+
+    flops = 4.0 * w.head_dim * w.hq * info["visible_pairs"]
+    return dict(name="prefill", w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="packed tokens",
+                flops=flops, bytes=None, bound="mfma", plan_us=plan_us, kernel="attn_kernel<bf16,128,2,prefill>")
+
+
+def decode_case():
+    w = synth.config4()
+    t0 = time.perf_counter()
+    plan = ta.plan_for(w.desc)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    plan.upload()
+    t = {k: v.cuda() for k, v in w.tensors.items()}
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((w.hq, t["q"].shape[0]), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(ta.decode_scratch_bytes(plan, w.hq, w.head_dim) + 256, dtype=torch.uint8, device="cuda")
+    info = plan.info
+    rows = plan.export("decode_rows")  # main_start, main_len, suffix_start, suffix_len, position
+
+    def run():
+        ta.decode(plan, t["q"], t["k_main"], t["v_main"], t["k_suffix"], t["v_suffix"], scale=w.scale,
+                  out=o, lse=lse, scratch=scratch)
+
+    # distinct keys any branch reads: per page the longest visible main prefix, plus every suffix
+    main_keys = 0
+    for p in range(w.desc.n_pages):
+        sel = w.desc.br_page == p
+        if sel.any():
+            main_keys += int(rows[sel, 1].max())
+    suffix_keys = int(rows[:, 3].sum())
+    e = elt(w.dtype)
+    kv_bytes = (main_keys + suffix_keys) * w.hkv * w.head_dim * 2 * e
+    qo_bytes = info["n_rows"] * w.hq * w.head_dim * 2 * e + info["n_rows"] * w.hq * 4
+    flops = 4.0 * w.head_dim * w.hq * info["visible_pairs"]
+    return dict(name="decode", w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="query tokens",
+                flops=flops, bytes=kv_bytes + qo_bytes, bound="hbm", plan_us=plan_us,
+                kernel="attn_kernel<bf16,128,2,decode> + merge_kernel")
+
+
+def verify_case():
+    w = synth.config5()
+    t0 = time.perf_counter()
+    plan = ta.plan_for(w.desc)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    plan.upload()
+    t = {k: v.cuda() for k, v in w.tensors.items()}
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((w.hq, t["q"].shape[0]), dtype=torch.float32, device="cuda")
+    info = plan.info
+
+    def run():
+        ta.verify(plan, t["q"], t["k_ctx"], t["v_ctx"], t["k_tree"], t["v_tree"], scale=w.scale, out=o, lse=lse)
+
+    e = elt(w.dtype)
+    flops = 4.0 * w.head_dim * w.hq * info["visible_pairs"]
+    bytes_ = ((info["n_keys_a"] + info["n_keys_b"]) * w.hkv * w.head_dim * 2 * e
+              + info["n_rows"] * w.hq * w.head_dim * 2 * e)
+    return dict(name="verify", w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="draft nodes",
+                flops=flops, bytes=bytes_, bound="mfma", plan_us=plan_us, kernel="attn_kernel<bf16,128,2,verify>")
+
+
+def traffic_for(kernel_name):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if
+    they were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "tree_structured_attention_amd", "csrc", "attn_kernels.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    entry = rec.get("kernels", {}).get(kernel_name)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s: float):
+    """The fp64 oracle on a bounded, evenly spread sample of the prefill rows."""
+    import oracle  # test infrastructure: used only for this reported baseline
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = synth.config2()
+    P = int(w.desc.prefix_len[0])
+    L = w.desc.layout_len
+    C = w.desc.content_len
+    T = w.desc.total_tokens()
+    t0 = time.perf_counter()
+    mask = oracle.ancestor_mask_page(P, L, C)
+    order = np.random.default_rng(0).permutation(T)
+    done = 0
+    block = 256
+    while done < T and time.perf_counter() - t0 < budget_s:
+        rows = np.sort(order[done:done + block])
+        oracle.masked_attention(w.tensors["q"][rows], w.tensors["k"], w.tensors["v"], mask[rows], w.scale)
+        done += len(rows)
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "packed tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {T} rows of the one-page prefill workload (random rows, all 16 heads, "
+                      f"fp64 numpy with the dense ancestor mask), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "verify"], default=None,
+                    help="time one entry point only (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the tree attention path has no multi-GPU mode "
+              "(pages shard across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    log("[bench] generating inputs")
+    cases = []
+    for name, fn in (("prefill", prefill_case), ("decode", decode_case), ("verify", verify_case)):
+        if args.only is None or args.only == name:
+            cases.append(fn())
+            log(f"[bench] {name}: {cases[-1]['w'].name} ready")
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for c in cases:
+            c["run"]()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(cases) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        for i, c in enumerate(cases):
+            c["run"]()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"[bench] timed {args.steps} steps in {wall * 1e3:.1f} ms")
+
+    per_case = {}
+    for i, c in enumerate(cases):
+        ms = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
+        avg = float(np.mean(ms))
+        sec = avg / 1e3
+        r = {"workload": c["w"].name, "kernel": c["kernel"], "ms_avg": avg, "ms_min": float(np.min(ms)),
+             "ms_median": float(np.median(ms)), f"{c['unit'].replace(' ', '_')}_per_s": c["unit_count"] / sec,
+             "tflops": c["flops"] / sec / 1e12, "plan_build_us": c["plan_us"]}
+        if c["bound"] == "mfma":
+            ach = c["flops"] / sec / 1e12
+            r["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic_for(c["name"])}
+        else:
+            ach = c["bytes"] / sec / 1e9
+            r["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": ach / PEAK_HBM_GBS, "traffic": traffic_for(c["name"])}
+        if c["bytes"] is not None:
+            r["gbs"] = c["bytes"] / sec / 1e9
+        per_case[c["name"]] = r
+        log(f"[bench] {c['name']}: {avg * 1e3:.1f} us  {json.dumps(r['roofline'])}")
+
+    step_ms = sum(per_case[c["name"]]["ms_avg"] for c in cases)
+    dominant = max(per_case, key=lambda k: per_case[k]["ms_avg"])
+    head = per_case.get("prefill") or per_case[dominant]
+    value = head.get("packed_tokens_per_s") or next(v for k, v in head.items() if k.endswith("_per_s"))
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "packed tokens/s" if "prefill" in per_case else "units/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill 1 page P=4096 N=24 L=12 lognormal C (8,772 tokens) + decode 16 pages x 24 "
+                               "branches P=4809 + verify 64 pages x 8 trees x 32 nodes; 16q/8kv heads, d=128",
+                   "prefill_tokens": per_case.get("prefill", {}).get("workload"),
+                   "parallelism": "single GPU"},
+        "roofline": dict(per_case[dominant]["roofline"], kernel=per_case[dominant]["kernel"]),
+        "entries": per_case,
+        "wall_ms_timed_region": wall * 1e3,
+    }
+    if "decode" in per_case:
+        out["decode_query_tokens_per_s"] = per_case["decode"]["query_tokens_per_s"]
+        out["decode_hbm_frac"] = per_case["decode"]["roofline"]["frac"]
+    if "prefill" in per_case:
+        out["prefill_mfma_frac"] = per_case["prefill"]["roofline"]["frac"]
+    if not args.no_cpu_baseline and args.only is None:
+        log("[bench] timing the CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
