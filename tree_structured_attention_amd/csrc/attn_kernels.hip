@@ -51,7 +51,18 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 // small device helpers
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float shfl_xor32(float x) { return __shfl_xor(x, 32, 64); }
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Row maximum / sum across the two lanes (l, l + 32) that share a query row.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -63,130 +74,80 @@ __device__ __forceinline__ int key_perm(int m) {
 // physical key 16 * (i / 8) + 8 * h + (i % 8).
 __device__ __forceinline__ int reg_key(int i, int h) { return 16 * (i >> 3) + 8 * h + (i & 7); }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+
+// Two fp32 -> bf16 (round to nearest even) in one packed convert.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
-  return uint32_t(__builtin_bit_cast(uint16_t, x)) | (uint32_t(__builtin_bit_cast(uint16_t, y)) << 16);
+  const f32x2v f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
 template <typename T>
-struct TileCfg;
-
+struct Elt;
 template <>
-struct TileCfg<__bf16> {
-  static constexpr int kElt = 2;
+struct Elt<__bf16> {
+  static constexpr int kBytes = 2;
 };
 template <>
-struct TileCfg<float> {
-  static constexpr int kElt = 4;
+struct Elt<float> {
+  static constexpr int kBytes = 4;
 };
 
-// LDS geometry for one 64-key tile of head_dim D.
+// LDS geometry of one 64-key tile: K and V row-major, one row per key, no
+// padding.  The 16-byte chunks of a row are XOR-swizzled,
+//   position = chunk ^ swz(row),  swz(row) = ((row % (C/2)) << 1) | ((row / (C/2)) % 2)
+// (C = chunks per row), so that the 32 K rows an MFMA operand read touches
+// and the 4 x 2 chunks of a transposing V read fall in distinct banks.
 template <typename T, int D>
-struct Lds {
-  static constexpr bool kBf = std::is_same<T, __bf16>::value;
-  // K tile row-major [64][D] with a 16-byte pad per row.
-  static constexpr int kKRow = D * TileCfg<T>::kElt + 16;
-  static constexpr int kKBytes = kKeyTile * kKRow;
-  // V tile: bf16 transposed [D][64] (+16 B pad); fp32 row-major [64][D] (+16 B).
-  static constexpr int kVRow = kBf ? (kKeyTile * 2 + 16) : (D * 4 + 16);
-  static constexpr int kVBytes = kBf ? D * kVRow : kKeyTile * kVRow;
-  static constexpr int kBytes = kKBytes + kVBytes;
+struct TileGeom {
+  static constexpr int kRowBytes = D * Elt<T>::kBytes;
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kTileBytes = kKeyTile * kRowBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes;  // K then V
+  __device__ static __forceinline__ int swz(int row) {
+    return ((row & (kChunks / 2 - 1)) << 1) | ((row / (kChunks / 2)) & 1);
+  }
+  // byte offset of (row, byte-in-row) inside a K or V tile
+  __device__ static __forceinline__ int at(int row, int byte) {
+    return row * kRowBytes + ((((byte >> 4) ^ swz(row)) << 4) | (byte & 15));
+  }
 };
 
-// ---------------------------------------------------------------------------
-// tile loader: global -> registers -> LDS
-// ---------------------------------------------------------------------------
+// Global -> LDS copy of one 64-key K/V tile with buffer loads that write LDS
+// directly.  The buffer resource covers only the keys of the segment still
+// to be read, so rows past its end load as zeros (no branches).
+template <typename T, int D, int NW>
+struct TileLoader {
+  using G = TileGeom<T, D>;
+  static constexpr int kRowsPerInst = 64 / G::kChunks;
+  static constexpr int kInsts = kKeyTile / (kRowsPerInst * NW);
+  static_assert(kInsts * kRowsPerInst * NW == kKeyTile, "tile split");
+  int voff[kInsts];  // per-lane byte offset into the tile's key rows
 
-template <typename T, int D, int NT>
-struct TileRegs {
-  static constexpr bool kBf = std::is_same<T, __bf16>::value;
-  // K: 16-byte chunks, D*elt/16 per key.
-  static constexpr int kKChunksPerKey = D * TileCfg<T>::kElt / 16;
-  static constexpr int kKChunks = kKeyTile * kKChunksPerKey;
-  static constexpr int kKPerThread = (kKChunks + NT - 1) / NT;
-  // V (bf16): units of 4 keys x 8 dims; V (fp32): 16-byte chunks like K.
-  static constexpr int kVUnits = kBf ? (kKeyTile / 4) * (D / 8) : kKChunks;
-  static constexpr int kVPerThread = (kVUnits + NT - 1) / NT;
-  static constexpr int kVLoads = kBf ? 4 : 1;
-  u32x4 k[kKPerThread];
-  u32x4 v[kVPerThread][kVLoads];
-
-  __device__ __forceinline__ void load(const unsigned char* kbase, const unsigned char* vbase, int t0, int t1,
-                                       int64_t row_stride_bytes, int tid) {
+  __device__ __forceinline__ void init(int lane, int wave, int64_t row_stride) {
 #pragma unroll
-    for (int j = 0; j < kKPerThread; ++j) {
-      const int c = tid + j * NT;
-      const int key = c / kKChunksPerKey, ch = c % kKChunksPerKey;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (c < kKChunks && t0 + key < t1)
-        val = *reinterpret_cast<const u32x4*>(kbase + int64_t(t0 + key) * row_stride_bytes + ch * 16);
-      k[j] = val;
-    }
-    if constexpr (kBf) {
-#pragma unroll
-      for (int j = 0; j < kVPerThread; ++j) {
-        const int u = tid + j * NT;
-        const int kg = u / (D / 8), dc = u % (D / 8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          u32x4 val = {0u, 0u, 0u, 0u};
-          const int key = 4 * kg + r;
-          if (u < kVUnits && t0 + key < t1)
-            val = *reinterpret_cast<const u32x4*>(vbase + int64_t(t0 + key) * row_stride_bytes + dc * 16);
-          v[j][r] = val;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kVPerThread; ++j) {
-        const int c = tid + j * NT;
-        const int key = c / kKChunksPerKey, ch = c % kKChunksPerKey;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (c < kVUnits && t0 + key < t1)
-          val = *reinterpret_cast<const u32x4*>(vbase + int64_t(t0 + key) * row_stride_bytes + ch * 16);
-        v[j][0] = val;
-      }
+    for (int j = 0; j < kInsts; ++j) {
+      const int row = (j * NW + wave) * kRowsPerInst + lane / G::kChunks;
+      const int chunk = (lane % G::kChunks) ^ G::swz(row);
+      voff[j] = int(row * row_stride) + chunk * 16;
     }
   }
 
-  __device__ __forceinline__ void store(unsigned char* lds, int tid) const {
-    using L = Lds<T, D>;
+  __device__ __forceinline__ void issue(unsigned char* stage, const unsigned char* kbase, const unsigned char* vbase,
+                                        int t0, int t1, int64_t row_stride, int wave) const {
+    const int rows = min(t1 - t0, kKeyTile);
+    const int nbytes = rows > 0 ? int(rows * row_stride) : 0;
+    __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase) + int64_t(t0) * row_stride, (short)0, nbytes, 0x00020000);
+    __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase) + int64_t(t0) * row_stride, (short)0, nbytes, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < kKPerThread; ++j) {
-      const int c = tid + j * NT;
-      if (c < kKChunks) {
-        const int key = c / kKChunksPerKey, ch = c % kKChunksPerKey;
-        *reinterpret_cast<u32x4*>(lds + key * L::kKRow + ch * 16) = k[j];
-      }
-    }
-    unsigned char* vl = lds + L::kKBytes;
-    if constexpr (kBf) {
-      // 4 keys x 8 dims -> for each dim e, 4 consecutive keys (8 bytes) of Vt[d].
-#pragma unroll
-      for (int j = 0; j < kVPerThread; ++j) {
-        const int u = tid + j * NT;
-        if (u < kVUnits) {
-          const int kg = u / (D / 8), dc = u % (D / 8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1;
-            const int sh = (e & 1) * 16;
-            const uint32_t k0 = (v[j][0][w] >> sh) & 0xffffu, k1 = (v[j][1][w] >> sh) & 0xffffu;
-            const uint32_t k2 = (v[j][2][w] >> sh) & 0xffffu, k3 = (v[j][3][w] >> sh) & 0xffffu;
-            u32x2 out = {k0 | (k1 << 16), k2 | (k3 << 16)};
-            *reinterpret_cast<u32x2*>(vl + (8 * dc + e) * L::kVRow + kg * 8) = out;
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kVPerThread; ++j) {
-        const int c = tid + j * NT;
-        if (c < kVUnits) {
-          const int key = c / kKChunksPerKey, ch = c % kKChunksPerKey;
-          *reinterpret_cast<u32x4*>(vl + key * L::kVRow + ch * 16) = v[j][0];
-        }
-      }
+    for (int j = 0; j < kInsts; ++j) {
+      const int row0 = (j * NW + wave) * kRowsPerInst;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + row0 * G::kRowBytes), 16, voff[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + G::kTileBytes + row0 * G::kRowBytes), 16,
+                                               voff[j], 0, 0, 0);
     }
   }
 };
@@ -196,19 +157,20 @@ struct TileRegs {
 // ---------------------------------------------------------------------------
 
 // GH query heads of one KV head per workgroup; 32 / GH tokens per wave; a
-// 64-token row tile therefore takes 2 * GH waves.
+// 64-token row tile therefore takes 2 * GH waves.  Two LDS stages: the tile
+// after the current one streams in while the current one is consumed, with
+// one barrier per tile.
 template <typename T, int D, int GH, int MODE>
 __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   constexpr bool kBf = std::is_same<T, __bf16>::value;
   constexpr int NW = 2 * GH;
-  constexpr int NT = 64 * NW;
   constexpr int TPW = 32 / GH;
   constexpr int kQSteps = kBf ? D / 16 : D / 2;  // MFMA k-steps over head_dim
   constexpr int kDB = D / 32;                    // 32-wide blocks of head_dim
-  using L = Lds<T, D>;
+  using G = TileGeom<T, D>;
   using QFrag = typename std::conditional<kBf, bf16x8, float>::type;
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * G::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -219,6 +181,26 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   const int head = kvh * p.group + int(blockIdx.y) * GH + (n % GH);
   const bool row_ok = tok < wi.nrows;
   const int row = wi.row0 + tok;
+
+  const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
+  const int n_b = (wi.b_hi - wi.b_lo + kKeyTile - 1) / kKeyTile;
+  const int n_tiles = n_a + n_b;
+  const int64_t kv_stride = int64_t(p.hkv) * D * Elt<T>::kBytes;
+  const int64_t head_off = int64_t(kvh) * D * Elt<T>::kBytes;
+  const unsigned char* ka = reinterpret_cast<const unsigned char*>(p.ka) + head_off;
+  const unsigned char* va = reinterpret_cast<const unsigned char*>(p.va) + head_off;
+  const unsigned char* kb = reinterpret_cast<const unsigned char*>(p.kb) + head_off;
+  const unsigned char* vb = reinterpret_cast<const unsigned char*>(p.vb) + head_off;
+  const int b_full = (wi.flags & kSegBFull) ? wi.b_hi : wi.b_lo;
+
+  TileLoader<T, D, NW> loader;
+  loader.init(lane, wave, kv_stride);
+  if (n_tiles > 0) {
+    if (n_a > 0)
+      loader.issue(lds, ka, va, wi.a_lo, wi.a_hi, kv_stride, wave);
+    else
+      loader.issue(lds, kb, vb, wi.b_lo, wi.b_hi, kv_stride, wave);
+  }
 
   int ra = 0, rb = 0;
   uint64_t rmask = 0;
@@ -251,28 +233,11 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[md][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const bool wave_active = wave * TPW < wi.nrows;
 
-  const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
-  const int n_b = (wi.b_hi - wi.b_lo + kKeyTile - 1) / kKeyTile;
-  const int n_tiles = n_a + n_b;
-  const int64_t kv_stride = int64_t(p.hkv) * D * TileCfg<T>::kElt;
-  const int64_t head_off = int64_t(kvh) * D * TileCfg<T>::kElt;
-  const unsigned char* ka = reinterpret_cast<const unsigned char*>(p.ka) + head_off;
-  const unsigned char* va = reinterpret_cast<const unsigned char*>(p.va) + head_off;
-  const unsigned char* kb = reinterpret_cast<const unsigned char*>(p.kb) + head_off;
-  const unsigned char* vb = reinterpret_cast<const unsigned char*>(p.vb) + head_off;
-  const int b_full = (wi.flags & kSegBFull) ? wi.b_hi : wi.b_lo;
-
-  TileRegs<T, D, NT> regs;
-  if (n_tiles > 0) {
-    if (n_a > 0)
-      regs.load(ka, va, wi.a_lo, wi.a_hi, kv_stride, tid);
-    else
-      regs.load(kb, vb, wi.b_lo, wi.b_hi, kv_stride, tid);
-  }
-
-  const unsigned char* kl = lds;
-  const unsigned char* vl = lds + L::kKBytes;
+  // Per-lane parts of the LDS read addresses (see TileGeom::at).
+  const int krow0 = key_perm(n);
+  const int m16 = lane & 15, grp = lane >> 4;
 
   for (int it = 0; it < n_tiles; ++it) {
     const bool seg_a = it < n_a;
@@ -280,18 +245,19 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
     const int t_hi = seg_a ? wi.a_hi : wi.b_hi;
     const int t_full = seg_a ? wi.a_full : b_full;
 
-    __syncthreads();
-    regs.store(lds, tid);
-    __syncthreads();
+    __syncthreads();  // tile `it` has landed; every wave is done with tile it-1
     if (it + 1 < n_tiles) {
       const int nx = it + 1;
+      unsigned char* stage = lds + (nx & 1) * G::kStageBytes;
       if (nx < n_a)
-        regs.load(ka, va, wi.a_lo + nx * kKeyTile, wi.a_hi, kv_stride, tid);
+        loader.issue(stage, ka, va, wi.a_lo + nx * kKeyTile, wi.a_hi, kv_stride, wave);
       else
-        regs.load(kb, vb, wi.b_lo + (nx - n_a) * kKeyTile, wi.b_hi, kv_stride, tid);
+        loader.issue(stage, kb, vb, wi.b_lo + (nx - n_a) * kKeyTile, wi.b_hi, kv_stride, wave);
     }
-    // waves without any valid row skip the math (the tile is still staged)
-    if (wave * TPW >= wi.nrows) continue;
+    if (!wave_active) continue;
+
+    const unsigned char* kl = lds + (it & 1) * G::kStageBytes;
+    const unsigned char* vl = kl + G::kTileBytes;
 
     // ---- S^T = K Q^T for two 32-key blocks ----
     f32x16 s[2];
@@ -299,17 +265,17 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
     for (int bk = 0; bk < 2; ++bk) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[bk][i] = 0.f;
-      const int krow = 32 * bk + key_perm(n);
+      const int krow = 32 * bk + krow0;
       if constexpr (kBf) {
 #pragma unroll
         for (int st = 0; st < kQSteps; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + krow * L::kKRow + (D * h + 16 * st));
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + G::at(krow, D * h + 16 * st));
           s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[bk], 0, 0, 0);
         }
       } else {
 #pragma unroll
         for (int st = 0; st < kQSteps; ++st) {
-          const float a = *reinterpret_cast<const float*>(kl + krow * L::kKRow + ((D / 2) * h + st) * 4);
+          const float a = *reinterpret_cast<const float*>(kl + G::at(krow, ((D / 2) * h + st) * 4));
           s[bk] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[st], s[bk], 0, 0, 0);
         }
       }
@@ -346,7 +312,7 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
     for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[bk][i]);
-    mt = fmaxf(mt, shfl_xor32(mt));
+    mt = pair_max(mt);
     const float m_new = fmaxf(m_run, mt);
     if (__any(m_new > m_run)) {
       const float alpha = (m_new > m_run) ? fast_exp2((m_run - m_new) * p.c) : 1.f;
@@ -379,10 +345,16 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(s[bk][8 * c2 + 2 * j], s[bk][8 * c2 + 2 * j + 1]);
           const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-          const int kcol = (32 * bk + 16 * c2 + 8 * h) * 2;
+          // transposing reads: lane m of each 16-lane group addresses
+          // V[key0 + m/4][d0 + 4 (m%4)]; lane i receives keys key0..key0+3 at d0 + i.
+          const int key0 = 32 * bk + 16 * c2 + 8 * (grp >> 1) + (m16 >> 2);
 #pragma unroll
           for (int md = 0; md < kDB; ++md) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(vl + (32 * md + n) * L::kVRow + kcol);
+            const int dbyte = 2 * (32 * md + 16 * (grp & 1) + 4 * (m16 & 3));
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vl + G::at(key0, dbyte)));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vl + G::at(key0 + 4, dbyte)));
+            const s16x4 both[2] = {lo, hi};
+            const bf16x8 a = __builtin_bit_cast(bf16x8, both);
             acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[md], 0, 0, 0);
           }
         }
@@ -392,7 +364,7 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
           const int key = 32 * bk + reg_key(i, h);
 #pragma unroll
           for (int md = 0; md < kDB; ++md) {
-            const float a = *reinterpret_cast<const float*>(vl + key * L::kVRow + (32 * md + n) * 4);
+            const float a = *reinterpret_cast<const float*>(vl + G::at(key, (32 * md + n) * 4));
             acc[md] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[bk][i], acc[md], 0, 0, 0);
           }
         }
@@ -401,7 +373,7 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   }
 
   // ---- epilogue ----
-  const float l_tot = l_run + shfl_xor32(l_run);
+  const float l_tot = pair_sum(l_run);
   if (!row_ok) return;
   if constexpr (MODE == kDecode) {
     const int64_t slot = int64_t(wi.out) + tok;
@@ -484,6 +456,26 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   }
   if (p.lse && lane == 0) p.lse[int64_t(head) * p.n_rows + row] = (mx + __log2f(l)) * 0.69314718055994531f;
 }
+
+// Explicit instantiations: every (dtype, head_dim, heads-per-workgroup, mode)
+// the launchers can select.
+#define TA_INSTANTIATE(T, D, GH)                                           \
+  template __global__ void attn_kernel<T, D, GH, kPrefill>(AttnParams); \
+  template __global__ void attn_kernel<T, D, GH, kVerify>(AttnParams);  \
+  template __global__ void attn_kernel<T, D, GH, kDecode>(AttnParams);
+TA_INSTANTIATE(__bf16, 32, 1)
+TA_INSTANTIATE(__bf16, 32, 2)
+TA_INSTANTIATE(__bf16, 64, 1)
+TA_INSTANTIATE(__bf16, 64, 2)
+TA_INSTANTIATE(__bf16, 128, 1)
+TA_INSTANTIATE(__bf16, 128, 2)
+TA_INSTANTIATE(float, 32, 1)
+TA_INSTANTIATE(float, 32, 2)
+TA_INSTANTIATE(float, 64, 1)
+TA_INSTANTIATE(float, 64, 2)
+TA_INSTANTIATE(float, 128, 1)
+TA_INSTANTIATE(float, 128, 2)
+#undef TA_INSTANTIATE
 
 // ---------------------------------------------------------------------------
 // host launchers
