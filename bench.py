@@ -173,6 +173,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "verify"], default=None,
                     help="time one entry point only (profiling runs)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before timing, run a plain device copy of this many MiB three times "
+                         "(reference for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the tree attention path has no multi-GPU mode "
@@ -182,6 +185,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.calib_copy_mib > 0:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+        del src, dst
     log("[bench] generating inputs")
     cases = []
     for name, fn in (("prefill", prefill_case), ("decode", decode_case), ("verify", verify_case)):
