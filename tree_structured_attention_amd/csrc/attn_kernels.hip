@@ -96,9 +96,13 @@ struct Elt<float> {
 
 // LDS geometry of one 64-key tile: K and V row-major, one row per key, no
 // padding.  The 16-byte chunks of a row are XOR-swizzled,
-//   position = chunk ^ swz(row),  swz(row) = ((row % (C/2)) << 1) | ((row / (C/2)) % 2)
-// (C = chunks per row), so that the 32 K rows an MFMA operand read touches
-// and the 4 x 2 chunks of a transposing V read fall in distinct banks.
+//   position = chunk ^ swz(row),
+// with swz a bijection of the low row bits (for 16 chunks per row: the
+// 4-bit row index rotated by 2).  Then the 16 K rows of an MFMA operand read
+// land in 16 different chunk positions, and in a transposing V read the two
+// 16-lane groups that share 4 rows touch 16 distinct positions (no bank
+// conflicts).  swz depends only on row % 16, so whole 16-row steps are plain
+// immediate offsets.
 template <typename T, int D>
 struct TileGeom {
   static constexpr int kRowBytes = D * Elt<T>::kBytes;
@@ -106,7 +110,9 @@ struct TileGeom {
   static constexpr int kTileBytes = kKeyTile * kRowBytes;
   static constexpr int kStageBytes = 2 * kTileBytes;  // K then V
   __device__ static __forceinline__ int swz(int row) {
-    return ((row & (kChunks / 2 - 1)) << 1) | ((row / (kChunks / 2)) & 1);
+    if constexpr (kChunks == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else if constexpr (kChunks == 8) return ((row & 1) << 2) | ((row >> 1) & 3);
+    else return ((row & 1) << 1) | ((row >> 1) & 1);
   }
   // byte offset of (row, byte-in-row) inside a K or V tile
   __device__ static __forceinline__ int at(int row, int byte) {
@@ -152,184 +158,124 @@ struct TileLoader {
   }
 };
 
-// ---------------------------------------------------------------------------
-// the attention kernel
-// ---------------------------------------------------------------------------
-
-// GH query heads of one KV head per workgroup; 32 / GH tokens per wave; a
-// 64-token row tile therefore takes 2 * GH waves.  Two LDS stages: the tile
-// after the current one streams in while the current one is consumed, with
-// one barrier per tile.
-template <typename T, int D, int GH, int MODE>
-__global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
-  constexpr bool kBf = std::is_same<T, __bf16>::value;
-  constexpr int NW = 2 * GH;
-  constexpr int TPW = 32 / GH;
-  constexpr int kQSteps = kBf ? D / 16 : D / 2;  // MFMA k-steps over head_dim
-  constexpr int kDB = D / 32;                    // 32-wide blocks of head_dim
+// Per-lane state of one wave: its 32 query rows (lane % 32) and the running
+// softmax of each.
+template <typename T, int D, int MODE>
+struct RowState {
+  static constexpr bool kBf = std::is_same<T, __bf16>::value;
+  static constexpr int kQSteps = kBf ? D / 16 : D / 2;  // MFMA k-steps over head_dim
+  static constexpr int kDB = D / 32;                    // 32-wide blocks of head_dim
   using G = TileGeom<T, D>;
   using QFrag = typename std::conditional<kBf, bf16x8, float>::type;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * G::kStageBytes];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, n = lane & 31;
-  const int kvh = int(blockIdx.x % unsigned(p.hkv));
-  const WorkItem wi = p.work[blockIdx.x / unsigned(p.hkv)];
-  const int tok = wave * TPW + n / GH;
-  const int head = kvh * p.group + int(blockIdx.y) * GH + (n % GH);
-  const bool row_ok = tok < wi.nrows;
-  const int row = wi.row0 + tok;
-
-  const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
-  const int n_b = (wi.b_hi - wi.b_lo + kKeyTile - 1) / kKeyTile;
-  const int n_tiles = n_a + n_b;
-  const int64_t kv_stride = int64_t(p.hkv) * D * Elt<T>::kBytes;
-  const int64_t head_off = int64_t(kvh) * D * Elt<T>::kBytes;
-  const unsigned char* ka = reinterpret_cast<const unsigned char*>(p.ka) + head_off;
-  const unsigned char* va = reinterpret_cast<const unsigned char*>(p.va) + head_off;
-  const unsigned char* kb = reinterpret_cast<const unsigned char*>(p.kb) + head_off;
-  const unsigned char* vb = reinterpret_cast<const unsigned char*>(p.vb) + head_off;
-  const int b_full = (wi.flags & kSegBFull) ? wi.b_hi : wi.b_lo;
-
-  TileLoader<T, D, NW> loader;
-  loader.init(lane, wave, kv_stride);
-  if (n_tiles > 0) {
-    if (n_a > 0)
-      loader.issue(lds, ka, va, wi.a_lo, wi.a_hi, kv_stride, wave);
-    else
-      loader.issue(lds, kb, vb, wi.b_lo, wi.b_hi, kv_stride, wave);
-  }
-
-  int ra = 0, rb = 0;
-  uint64_t rmask = 0;
-  if (row_ok) {
-    ra = p.row_a[row];
-    rb = p.row_b[row];
-    if constexpr (MODE == kVerify) rmask = p.row_mask[row];
-  }
-
-  // Q fragment: lane half h holds dims [(D/2) h, (D/2)(h+1)) of its row.
   QFrag qf[kQSteps];
-  {
-    const T* qrow = reinterpret_cast<const T*>(p.q) + (int64_t(row) * p.hq + head) * D + (D / 2) * h;
+  f32x16 acc[kDB];
+  float m_used;  // running maximum of the raw scores used as the exp2 base
+  float l_run;   // this lane's half of the row sum
+  int koff[kBf ? kQSteps : 1];
+  int voff[kBf ? 2 * kDB : 1];
+  int h, n, row, ra, rb;
+  uint64_t rmask;
+  bool row_ok;
+  float c, tau;
+
+  __device__ __forceinline__ void init_offsets(int lane) {
     if constexpr (kBf) {
+      const int krow0 = key_perm(n);
 #pragma unroll
-      for (int s = 0; s < kQSteps; ++s) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (row_ok) raw = *reinterpret_cast<const u32x4*>(qrow + 8 * s);
-        qf[s] = __builtin_bit_cast(bf16x8, raw);
-      }
-    } else {
+      for (int st = 0; st < kQSteps; ++st) koff[st] = G::at(krow0, D * h + 16 * st);
+      const int m16 = lane & 15, grp = lane >> 4;
+      // transposing reads: lane m of each 16-lane group addresses
+      // V[key0 + m/4][d0 + 4 (m%4)]; lane i receives keys key0..key0+3 at d0 + i.
 #pragma unroll
-      for (int s = 0; s < kQSteps; ++s) qf[s] = row_ok ? qrow[s] : 0.f;
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int md = 0; md < kDB; ++md) {
+          const int key = 8 * (grp >> 1) + 4 * r + (m16 >> 2);
+          const int dbyte = 2 * (32 * md + 16 * (grp & 1) + 4 * (m16 & 3));
+          voff[r * kDB + md] = G::at(key, dbyte);
+        }
     }
   }
 
-  f32x16 acc[kDB];
-#pragma unroll
-  for (int md = 0; md < kDB; ++md)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[md][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const bool wave_active = wave * TPW < wi.nrows;
-
-  // Per-lane parts of the LDS read addresses (see TileGeom::at).
-  const int krow0 = key_perm(n);
-  const int m16 = lane & 15, grp = lane >> 4;
-
-  for (int it = 0; it < n_tiles; ++it) {
-    const bool seg_a = it < n_a;
-    const int t0 = seg_a ? wi.a_lo + it * kKeyTile : wi.b_lo + (it - n_a) * kKeyTile;
-    const int t_hi = seg_a ? wi.a_hi : wi.b_hi;
-    const int t_full = seg_a ? wi.a_full : b_full;
-
-    __syncthreads();  // tile `it` has landed; every wave is done with tile it-1
-    if (it + 1 < n_tiles) {
-      const int nx = it + 1;
-      unsigned char* stage = lds + (nx & 1) * G::kStageBytes;
-      if (nx < n_a)
-        loader.issue(stage, ka, va, wi.a_lo + nx * kKeyTile, wi.a_hi, kv_stride, wave);
-      else
-        loader.issue(stage, kb, vb, wi.b_lo + (nx - n_a) * kKeyTile, wi.b_hi, kv_stride, wave);
-    }
-    if (!wave_active) continue;
-
-    const unsigned char* kl = lds + (it & 1) * G::kStageBytes;
-    const unsigned char* vl = kl + G::kTileBytes;
-
-    // ---- S^T = K Q^T for two 32-key blocks ----
+  // One 64-key tile from LDS (K at kl, V at vl).
+  __device__ __forceinline__ void consume(const unsigned char* kl, const unsigned char* vl, int t0, int t_hi,
+                                          bool seg_a, bool masked) {
+    // ---- S^T = K Q^T for two 32-key blocks (interleaved chains) ----
     f32x16 s[2];
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
+    for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[bk][i] = 0.f;
-      const int krow = 32 * bk + krow0;
-      if constexpr (kBf) {
+    if constexpr (kBf) {
 #pragma unroll
-        for (int st = 0; st < kQSteps; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + G::at(krow, D * h + 16 * st));
+      for (int st = 0; st < kQSteps; ++st)
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + koff[st] + 32 * bk * G::kRowBytes);
           s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[bk], 0, 0, 0);
         }
-      } else {
+    } else {
+      const int krow0 = key_perm(n);
 #pragma unroll
-        for (int st = 0; st < kQSteps; ++st) {
-          const float a = *reinterpret_cast<const float*>(kl + G::at(krow, ((D / 2) * h + st) * 4));
+      for (int st = 0; st < kQSteps; ++st)
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk) {
+          const float a = *reinterpret_cast<const float*>(kl + G::at(32 * bk + krow0, ((D / 2) * h + st) * 4));
           s[bk] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[st], s[bk], 0, 0, 0);
         }
-      }
     }
 
-    // ---- visibility (only tiles that reach past the all-visible prefix) ----
-    if (t0 + kKeyTile > t_full) {
+    // ---- visibility: selection to -inf, only on tiles that need it ----
+    if (masked) {
+      const int kbase = t0 + 8 * h;
 #pragma unroll
-      for (int bk = 0; bk < 2; ++bk) {
+      for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = t0 + 32 * bk + reg_key(i, h);
+          const int key = kbase + 32 * bk + 16 * (i >> 3) + (i & 7);
           bool vis = key < t_hi;
-          if (row_ok) {
-            if (seg_a) {
-              if constexpr (MODE != kVerify) vis = vis && key < ra;
-            } else {
-              if constexpr (MODE == kPrefill) {
-                vis = vis && key >= rb && key <= row;
-              } else if constexpr (MODE == kVerify) {
-                const unsigned rel = unsigned(key - rb);
-                vis = vis && rel < 64u && ((rmask >> (rel & 63u)) & 1ull);
-              }
+          if (seg_a) {
+            if constexpr (MODE != kVerify) vis = vis & (!row_ok | (key < ra));
+          } else {
+            if constexpr (MODE == kPrefill) {
+              vis = vis & (!row_ok | ((key >= rb) & (key <= row)));
+            } else if constexpr (MODE == kVerify) {
+              const unsigned rel = unsigned(key - rb);
+              const uint32_t word = rel < 32u ? uint32_t(rmask) : uint32_t(rmask >> 32);
+              vis = vis & (!row_ok | ((rel < 64u) & (((word >> (rel & 31u)) & 1u) != 0u)));
             }
           }
           s[bk][i] = vis ? s[bk][i] : -INFINITY;
         }
-      }
     }
 
-    // ---- online softmax ----
+    // ---- online softmax; the exp2 base moves only when a row's maximum
+    // grows by more than 2^8, so P stays <= 256 and the O rescale is rare ----
     float mt = s[0][0];
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[bk][i]);
     mt = pair_max(mt);
-    const float m_new = fmaxf(m_run, mt);
-    if (__any(m_new > m_run)) {
-      const float alpha = (m_new > m_run) ? fast_exp2((m_run - m_new) * p.c) : 1.f;
+    const bool grow = mt > m_used + tau;
+    if (__any(grow)) {
+      const float m_new = grow ? mt : m_used;
+      const float alpha = grow ? fast_exp2((m_used - m_new) * c) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int md = 0; md < kDB; ++md)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[md][i] *= alpha;
+      m_used = m_new;
     }
-    m_run = m_new;
-    const float mb = (m_new == -INFINITY) ? 0.f : m_new * p.c;
+    const float mb = (m_used == -INFINITY) ? 0.f : m_used * c;
     float ls = 0.f;
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(fmaf(s[bk][i], p.c, -mb));
+        const float e = fast_exp2(fmaf(s[bk][i], c, -mb));
         s[bk][i] = e;
         ls += e;
       }
@@ -345,14 +291,11 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(s[bk][8 * c2 + 2 * j], s[bk][8 * c2 + 2 * j + 1]);
           const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-          // transposing reads: lane m of each 16-lane group addresses
-          // V[key0 + m/4][d0 + 4 (m%4)]; lane i receives keys key0..key0+3 at d0 + i.
-          const int key0 = 32 * bk + 16 * c2 + 8 * (grp >> 1) + (m16 >> 2);
+          const unsigned char* vb = vl + (32 * bk + 16 * c2) * G::kRowBytes;
 #pragma unroll
           for (int md = 0; md < kDB; ++md) {
-            const int dbyte = 2 * (32 * md + 16 * (grp & 1) + 4 * (m16 & 3));
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vl + G::at(key0, dbyte)));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vl + G::at(key0 + 4, dbyte)));
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + voff[md]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + voff[kDB + md]));
             const s16x4 both[2] = {lo, hi};
             const bf16x8 a = __builtin_bit_cast(bf16x8, both);
             acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[md], 0, 0, 0);
@@ -371,10 +314,128 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
       }
     }
   }
+};
+
+// ---------------------------------------------------------------------------
+// the attention kernel
+// ---------------------------------------------------------------------------
+
+// GH query heads of one KV head per workgroup; 32 / GH tokens per wave; a
+// 64-token row tile therefore takes 2 * GH waves.  Two LDS stages: the tile
+// after the current one streams in while the current one is consumed, with
+// one barrier per tile.  Tiles are taken in four runs (segment A fully
+// visible, segment A masked, segment B fully visible, segment B masked); the
+// per-row visibility test runs only in the masked runs.
+template <typename T, int D, int GH, int MODE>
+__global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
+  constexpr bool kBf = std::is_same<T, __bf16>::value;
+  constexpr int NW = 2 * GH;
+  constexpr int TPW = 32 / GH;
+  using G = TileGeom<T, D>;
+  using RS = RowState<T, D, MODE>;
+  constexpr int kQSteps = RS::kQSteps;
+  constexpr int kDB = RS::kDB;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * G::kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int kvh = int(blockIdx.x % unsigned(p.hkv));
+  const WorkItem wi = p.work[blockIdx.x / unsigned(p.hkv)];
+
+  const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
+  const int n_b = (wi.b_hi - wi.b_lo + kKeyTile - 1) / kKeyTile;
+  const int n_tiles = n_a + n_b;
+  // tiles [0, fa) of segment A and [n_a, n_a + fb) of segment B need no mask
+  const int fa = min(n_a, max(0, wi.a_full - wi.a_lo) / kKeyTile);
+  const int fb = (wi.flags & kSegBFull) ? (wi.b_hi - wi.b_lo) / kKeyTile : 0;
+  const int64_t kv_stride = int64_t(p.hkv) * D * Elt<T>::kBytes;
+  const int64_t head_off = int64_t(kvh) * D * Elt<T>::kBytes;
+  const unsigned char* ka = reinterpret_cast<const unsigned char*>(p.ka) + head_off;
+  const unsigned char* va = reinterpret_cast<const unsigned char*>(p.va) + head_off;
+  const unsigned char* kb = reinterpret_cast<const unsigned char*>(p.kb) + head_off;
+  const unsigned char* vb = reinterpret_cast<const unsigned char*>(p.vb) + head_off;
+
+  TileLoader<T, D, NW> loader;
+  loader.init(lane, wave, kv_stride);
+  if (n_tiles > 0) {
+    if (n_a > 0)
+      loader.issue(lds, ka, va, wi.a_lo, wi.a_hi, kv_stride, wave);
+    else
+      loader.issue(lds, kb, vb, wi.b_lo, wi.b_hi, kv_stride, wave);
+  }
+
+  RS rs;
+  rs.h = lane >> 5;
+  rs.n = lane & 31;
+  const int tok = wave * TPW + rs.n / GH;
+  const int head = kvh * p.group + int(blockIdx.y) * GH + (rs.n % GH);
+  rs.row_ok = tok < wi.nrows;
+  rs.row = wi.row0 + tok;
+  rs.ra = 0;
+  rs.rb = 0;
+  rs.rmask = 0;
+  if (rs.row_ok) {
+    rs.ra = p.row_a[rs.row];
+    rs.rb = p.row_b[rs.row];
+    if constexpr (MODE == kVerify) rs.rmask = p.row_mask[rs.row];
+  }
+  rs.c = p.c;
+  rs.tau = 8.f / p.c;
+  rs.m_used = -INFINITY;
+  rs.l_run = 0.f;
+  rs.init_offsets(lane);
+
+  // Q fragment: lane half h holds dims [(D/2) h, (D/2)(h+1)) of its row.
+  {
+    const T* qrow = reinterpret_cast<const T*>(p.q) + (int64_t(rs.row) * p.hq + head) * D + (D / 2) * rs.h;
+    if constexpr (kBf) {
+#pragma unroll
+      for (int s = 0; s < kQSteps; ++s) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (rs.row_ok) raw = *reinterpret_cast<const u32x4*>(qrow + 8 * s);
+        rs.qf[s] = __builtin_bit_cast(bf16x8, raw);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < kQSteps; ++s) rs.qf[s] = rs.row_ok ? qrow[s] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int md = 0; md < kDB; ++md)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rs.acc[md][i] = 0.f;
+  const bool wave_active = wave * TPW < wi.nrows;
+
+  // Four runs: seg A unmasked, seg A masked, seg B unmasked, seg B masked.
+  int it = 0;
+#pragma unroll 1
+  for (int run = 0; run < 4; ++run) {
+    const bool seg_a = run < 2;
+    const int run_end = run == 0 ? fa : run == 1 ? n_a : run == 2 ? n_a + fb : n_tiles;
+    const int t_hi = seg_a ? wi.a_hi : wi.b_hi;
+#pragma unroll 1
+    for (; it < run_end; ++it) {
+      const int t0 = seg_a ? wi.a_lo + it * kKeyTile : wi.b_lo + (it - n_a) * kKeyTile;
+      __syncthreads();  // tile `it` has landed; every wave is done with tile it-1
+      if (it + 1 < n_tiles) {
+        const int nx = it + 1;
+        unsigned char* stage = lds + (nx & 1) * G::kStageBytes;
+        if (nx < n_a)
+          loader.issue(stage, ka, va, wi.a_lo + nx * kKeyTile, wi.a_hi, kv_stride, wave);
+        else
+          loader.issue(stage, kb, vb, wi.b_lo + (nx - n_a) * kKeyTile, wi.b_hi, kv_stride, wave);
+      }
+      if (!wave_active) continue;
+      const unsigned char* kl = lds + (it & 1) * G::kStageBytes;
+      rs.consume(kl, kl + G::kTileBytes, t0, t_hi, seg_a, (run & 1) != 0);
+    }
+  }
 
   // ---- epilogue ----
-  const float l_tot = pair_sum(l_run);
-  if (!row_ok) return;
+  const float l_tot = pair_sum(rs.l_run);
+  if (!rs.row_ok) return;
+  const int h = rs.h;
   if constexpr (MODE == kDecode) {
     const int64_t slot = int64_t(wi.out) + tok;
     const int64_t idx = slot * p.hq + head;
@@ -384,32 +445,33 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * md + 8 * g + 4 * h;
-        float4 vv = {acc[md][4 * g], acc[md][4 * g + 1], acc[md][4 * g + 2], acc[md][4 * g + 3]};
+        float4 vv = {rs.acc[md][4 * g], rs.acc[md][4 * g + 1], rs.acc[md][4 * g + 2], rs.acc[md][4 * g + 3]};
         *reinterpret_cast<float4*>(dst + d0) = vv;
       }
     if (h == 0) {
-      float2 ml = {m_run == -INFINITY ? -INFINITY : m_run * p.c, l_tot};
+      float2 ml = {rs.m_used == -INFINITY ? -INFINITY : rs.m_used * p.c, l_tot};
       *reinterpret_cast<float2*>(p.part_ml + idx * 2) = ml;
     }
   } else {
     const float inv = 1.f / l_tot;
-    T* dst = reinterpret_cast<T*>(p.o) + (int64_t(row) * p.hq + head) * D;
+    T* dst = reinterpret_cast<T*>(p.o) + (int64_t(rs.row) * p.hq + head) * D;
 #pragma unroll
     for (int md = 0; md < kDB; ++md)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * md + 8 * g + 4 * h;
         if constexpr (kBf) {
-          u32x2 w = {pack_bf16x2(acc[md][4 * g] * inv, acc[md][4 * g + 1] * inv),
-                     pack_bf16x2(acc[md][4 * g + 2] * inv, acc[md][4 * g + 3] * inv)};
+          u32x2 w = {pack_bf16x2(rs.acc[md][4 * g] * inv, rs.acc[md][4 * g + 1] * inv),
+                     pack_bf16x2(rs.acc[md][4 * g + 2] * inv, rs.acc[md][4 * g + 3] * inv)};
           *reinterpret_cast<u32x2*>(dst + d0) = w;
         } else {
-          float4 vv = {acc[md][4 * g] * inv, acc[md][4 * g + 1] * inv, acc[md][4 * g + 2] * inv,
-                       acc[md][4 * g + 3] * inv};
+          float4 vv = {rs.acc[md][4 * g] * inv, rs.acc[md][4 * g + 1] * inv, rs.acc[md][4 * g + 2] * inv,
+                       rs.acc[md][4 * g + 3] * inv};
           *reinterpret_cast<float4*>(dst + d0) = vv;
         }
       }
-    if (p.lse && h == 0) p.lse[int64_t(head) * p.n_rows + row] = (m_run * p.c + __log2f(l_tot)) * 0.69314718055994531f;
+    if (p.lse && h == 0)
+      p.lse[int64_t(head) * p.n_rows + rs.row] = (rs.m_used * p.c + __log2f(l_tot)) * 0.69314718055994531f;
   }
 }
 
