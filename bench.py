@@ -44,23 +44,29 @@ def elt(dtype):
     return 2 if dtype == torch.bfloat16 else 4
 
 
+def scratch_for(plan, w):
+    n = ta.scratch_bytes(plan, w.hq, w.head_dim)
+    return torch.empty(n + 256, dtype=torch.uint8, device="cuda") if n else None
+
+
 def prefill_case():
     w = synth.config2()
     t0 = time.perf_counter()
-    plan = ta.plan_for(w.desc)
+    plan = ta.plan_for(w.desc).balance(w.hkv)
     plan_us = (time.perf_counter() - t0) * 1e6
     plan.upload()
     t = {k: v.cuda() for k, v in w.tensors.items()}
     o = torch.empty_like(t["q"])
     lse = torch.empty((w.hq, t["q"].shape[0]), dtype=torch.float32, device="cuda")
+    scratch = scratch_for(plan, w)
     info = plan.info
 
     def run():
-        ta.prefill(plan, t["q"], t["k"], t["v"], scale=w.scale, out=o, lse=lse)
+        ta.prefill(plan, t["q"], t["k"], t["v"], scale=w.scale, out=o, lse=lse, scratch=scratch)
 
     flops = 4.0 * w.head_dim * w.hq * info["visible_pairs"]
     return dict(name="prefill", w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="packed tokens",
-                flops=flops, bytes=None, bound="mfma", plan_us=plan_us, kernel="attn_kernel<bf16,128,2,prefill>")
+                flops=flops, bytes=None, bound="mfma", plan_us=plan_us, kernel="attn_kernel<bf16,128,2,prefill> (+ merge_kernel for split tiles)")
 
 
 def decode_case():
@@ -72,7 +78,7 @@ def decode_case():
     t = {k: v.cuda() for k, v in w.tensors.items()}
     o = torch.empty_like(t["q"])
     lse = torch.empty((w.hq, t["q"].shape[0]), dtype=torch.float32, device="cuda")
-    scratch = torch.empty(ta.decode_scratch_bytes(plan, w.hq, w.head_dim) + 256, dtype=torch.uint8, device="cuda")
+    scratch = scratch_for(plan, w)
     info = plan.info
     rows = plan.export("decode_rows")  # main_start, main_len, suffix_start, suffix_len, position
 
@@ -99,16 +105,18 @@ def decode_case():
 def verify_case():
     w = synth.config5()
     t0 = time.perf_counter()
-    plan = ta.plan_for(w.desc)
+    plan = ta.plan_for(w.desc).balance(w.hkv)
     plan_us = (time.perf_counter() - t0) * 1e6
     plan.upload()
     t = {k: v.cuda() for k, v in w.tensors.items()}
     o = torch.empty_like(t["q"])
     lse = torch.empty((w.hq, t["q"].shape[0]), dtype=torch.float32, device="cuda")
+    scratch = scratch_for(plan, w)
     info = plan.info
 
     def run():
-        ta.verify(plan, t["q"], t["k_ctx"], t["v_ctx"], t["k_tree"], t["v_tree"], scale=w.scale, out=o, lse=lse)
+        ta.verify(plan, t["q"], t["k_ctx"], t["v_ctx"], t["k_tree"], t["v_tree"], scale=w.scale, out=o, lse=lse,
+                  scratch=scratch)
 
     e = elt(w.dtype)
     flops = 4.0 * w.head_dim * w.hq * info["visible_pairs"]

@@ -68,7 +68,8 @@ extern "C" {
 #define TA_FIELD_DECODE_ROWS 6  /* decode:  [branches][5] main_start, main_len, suffix_start, suffix_len, position */
 #define TA_FIELD_VERIFY_MASK 7  /* verify:  [nodes] ancestor bitmask (bit j: node j of the same branch is an ancestor or itself) */
 #define TA_FIELD_VERIFY_ROWS 8  /* verify:  [nodes][4] ctx_start, ctx_len, tree_base (abs node 0 of the branch), position */
-#define TA_FIELD_WORK 9         /* any:     [work][8] the launch work list (diagnostic; order is not part of the contract) */
+#define TA_FIELD_WORK 9         /* any:     [work][10] the launch work list: row0, nrows, a_lo, a_full, a_hi, b_lo, b_hi,
+                                           partial slot (-1: direct), tile_lo, tile_hi (diagnostic; order is not contractual) */
 
 typedef struct ta_plan ta_plan; /* opaque, host-owned, immutable once built */
 
@@ -81,7 +82,7 @@ typedef struct ta_plan_info {
   int64_t n_keys_a;         /* tokens the first key buffer must hold (k / k_main / k_ctx) */
   int64_t n_keys_b;         /* tokens the second key buffer must hold (k / k_suffix / k_tree) */
   int64_t workspace_bytes;  /* device workspace needed by tree_attn_plan_upload */
-  int64_t n_partials;       /* decode: partial (unit, row) slots per query head, else 0 */
+  int64_t n_partials;       /* fp32 partial slots per query head (decode chunks, split tiles); 0 if none */
   int64_t visible_pairs;    /* sum over rows of visible keys (algorithmic work, per head) */
   int64_t max_depth;        /* prefill: max D_PaDoc over pages; verify: max tree depth */
 } ta_plan_info;
@@ -154,6 +155,16 @@ int tree_attn_plan_info(const ta_plan* plan, ta_plan_info* out);
 int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t* dst,
                           int64_t cap, int64_t* n_written);
 
+/* Split the longest row tiles of a prefill or verify plan along their keys
+ * so that n_kv_heads x (work items) spread evenly over n_slots concurrent
+ * workgroups (MI355X: 2 per CU, 512).  Split pieces write fp32 partials
+ * that the launch merges by log-sum-exp in a fixed order, so results stay
+ * deterministic; tree_attn_scratch_bytes then becomes non-zero.  Optional;
+ * call before tree_attn_plan_upload, at most once.  No-op for decode plans
+ * (their work items are already key chunks).  Errors: INVALID_ARG for
+ * non-positive counts, STATE if the plan is uploaded or already balanced. */
+int tree_attn_plan_balance(ta_plan* plan, int32_t n_kv_heads, int32_t n_slots);
+
 /* Enqueue the asynchronous copy of the plan's device tables into
  * dev_workspace (>= info.workspace_bytes bytes, 256-byte aligned, caller
  * owned) on `stream`, and bind the plan to that workspace.  Kernels launched
@@ -163,22 +174,26 @@ int tree_attn_plan_upload(ta_plan* plan, void* dev_workspace, size_t bytes, void
 /* Wait for a pending upload, then free the host plan.  NULL is a no-op. */
 void tree_attn_plan_destroy(ta_plan* plan);
 
-/* Scratch bytes tree_attn_decode needs for these head counts. */
-int tree_attn_decode_scratch_bytes(const ta_plan* plan, int32_t hq, int32_t head_dim,
-                                   size_t* bytes);
+/* Scratch bytes a launch over this plan needs for these head counts (fp32
+ * partials of decode chunks and of split prefill/verify row tiles; 0 when
+ * the plan writes every output directly). */
+int tree_attn_scratch_bytes(const ta_plan* plan, int32_t hq, int32_t head_dim, size_t* bytes);
 
 /* Packed tree-varlen forward over a prefill plan.  q, o: [rows, Hq, d];
- * k, v: [rows, Hkv, d] (keys are the packed tokens themselves). */
+ * k, v: [rows, Hkv, d] (keys are the packed tokens themselves).
+ * scratch: >= tree_attn_scratch_bytes bytes, 256-byte aligned (may be NULL
+ * when that is 0). */
 int tree_attn_prefill(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
                       int32_t head_dim, float scale, const void* q, const void* k,
-                      const void* v, void* o, float* lse, void* stream);
+                      const void* v, void* o, float* lse, void* scratch,
+                      size_t scratch_bytes, void* stream);
 
 /* Cascade branch decode over a decode plan: pass 1 streams each page's main
  * KV once for all of its branches and query heads and each branch's suffix,
  * writing fp32 partials (m, l, acc) into `scratch`; pass 2 merges them by
  * log-sum-exp in a fixed order.  q, o: [n_branches, Hq, d];
  * k_main/v_main: [sum M_p, Hkv, d]; k_suffix/v_suffix: [sum (s_k+1), Hkv, d];
- * scratch: >= tree_attn_decode_scratch_bytes, 256-byte aligned. */
+ * scratch: >= tree_attn_scratch_bytes, 256-byte aligned. */
 int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
                      int32_t head_dim, float scale, const void* q, const void* k_main,
                      const void* v_main, const void* k_suffix, const void* v_suffix,
@@ -186,11 +201,13 @@ int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv
                      void* stream);
 
 /* Draft-tree verify over a verify plan.  q, o: [nodes, Hq, d];
- * k_ctx/v_ctx: [sum ctx_len, Hkv, d]; k_tree/v_tree: [nodes, Hkv, d]. */
+ * k_ctx/v_ctx: [sum ctx_len, Hkv, d]; k_tree/v_tree: [nodes, Hkv, d];
+ * scratch as for tree_attn_prefill. */
 int tree_attn_verify(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
                      int32_t head_dim, float scale, const void* q, const void* k_ctx,
                      const void* v_ctx, const void* k_tree, const void* v_tree,
-                     void* o, float* lse, void* stream);
+                     void* o, float* lse, void* scratch, size_t scratch_bytes,
+                     void* stream);
 
 /* Message of the last error on this thread ("" if none). */
 const char* tree_attn_last_error(void);

@@ -330,3 +330,57 @@ def test_verify_chain_equals_prefill_rows():
     o_v, l_v = gpu_verify(wv)
     close(o_v, o_pf[ctx:], (2e-2, 1e-2), "chain verify vs prefill o")
     close(l_v, l_pf[:, ctx:], (2e-3, 1e-3), "chain verify vs prefill lse")
+
+
+# --------------------------------------------------------------------------
+# plans balanced by key-range splits (fp32 partials + fixed-order merge)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,heads", [(torch.bfloat16, (16, 8, 128)), (torch.float32, (4, 2, 32))])
+def test_prefill_split_tiles_match_oracle(dtype, heads):
+    hq, hkv, d = heads
+    w = prefill_workload(None, None, None, hq=hq, hkv=hkv, d=d, dtype=dtype,
+                         pages=[(1500, [4, 0, 9], [300, 5, 700]), (700, [2], [90])], seed=21)
+    plan = ta.plan_for(w.desc).balance(hkv, 256)  # long tiles vs many slots: split
+    assert plan.info["n_partials"] > 0
+    plan.upload()
+    say(f"[prefill split] pieces={plan.info['n_work']} partial slots={plan.info['n_partials']}")
+    o, lse = gpu_prefill(w, plan)
+    ro, rl = oracle.prefill(w.desc, w.tensors["q"], w.tensors["k"], w.tensors["v"], w.scale)
+    close(o, ro, TOL[dtype], "split prefill o")
+    close(lse, rl, LSE_TOL[dtype], "split prefill lse")
+
+
+def test_prefill_config2_balanced_sampled_and_deterministic():
+    w = synth.config2()
+    plan = ta.plan_for(w.desc).balance(w.hkv).upload()
+    say(f"[prefill balanced] pieces={plan.info['n_work']} partial slots={plan.info['n_partials']}")
+    a = gpu_prefill(w, plan)
+    b = gpu_prefill(w, plan)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # same values as the unsplit plan, within the merge's fp32 rounding
+    c = gpu_prefill(w)
+    close(a[0], c[0], (2e-2, 1e-2), "balanced vs unsplit o")
+    rng = np.random.default_rng(31)
+    T = w.desc.total_tokens()
+    P = int(w.desc.prefix_len[0])
+    rows = np.array(sorted(set(rng.choice(T, 120, replace=False).tolist()) | {0, T - 1}))
+    mask = oracle.ancestor_mask_page(P, w.desc.layout_len, w.desc.content_len)[rows]
+    ro, rl = oracle.masked_attention(w.tensors["q"][rows], w.tensors["k"], w.tensors["v"], mask, w.scale)
+    close(a[0][rows], ro, TOL[w.dtype], "balanced config2 o")
+    close(a[1][:, rows], rl, LSE_TOL[w.dtype], "balanced config2 lse")
+
+
+def test_verify_split_tiles_match_oracle():
+    rng = np.random.default_rng(41)
+    trees = [(0, synth.random_tree_parents(rng, 32)), (0, synth.random_tree_parents(rng, 32)),
+             (1, synth.random_tree_parents(rng, 20))]
+    w = verify_workload([2500, 900], trees, seed=2)
+    plan = ta.plan_for(w.desc).balance(w.hkv, 256)
+    assert plan.info["n_partials"] > 0
+    plan.upload()
+    o, lse = gpu_verify(w, plan)
+    t = w.tensors
+    ro, rl = oracle.verify(w.desc, t["q"], t["k_ctx"], t["v_ctx"], t["k_tree"], t["v_tree"], w.scale)
+    close(o, ro, TOL[w.dtype], "split verify o")
+    close(lse, rl, LSE_TOL[w.dtype], "split verify lse")

@@ -15,7 +15,7 @@ from tree_structured_attention_amd import synth
 def test_library_exports_every_declared_symbol():
     L = ta.lib()
     declared = ta.header_symbols()
-    assert len(declared) == 13
+    assert len(declared) == 14
     for name in declared:
         assert hasattr(L, name), name
     assert L.tree_attn_version().decode().startswith("tree_attn")
@@ -160,13 +160,13 @@ def test_launch_errors_before_any_device_work():
         ((f32, 2, 1, 32, 0.2), ta.TA_ERR_STATE),        # valid, but never uploaded
     ]
     for (dt, hq, hkv, d, sc), code in cases:
-        rc = L.tree_attn_prefill(h, dt, hq, hkv, d, sc, p, p, p, p, None, None)
+        rc = L.tree_attn_prefill(h, dt, hq, hkv, d, sc, p, p, p, p, None, None, 0, None)
         assert rc == code, (dt, hq, hkv, d, sc, rc, ta.last_error())
     # NULL and misaligned tensors
-    assert L.tree_attn_prefill(h, bf, 2, 1, 32, 0.2, None, p, p, p, None, None) == ta.TA_ERR_INVALID_ARG
-    assert L.tree_attn_prefill(h, bf, 2, 1, 32, 0.2, fa.odd, p, p, p, None, None) == ta.TA_ERR_INVALID_ARG
+    assert L.tree_attn_prefill(h, bf, 2, 1, 32, 0.2, None, p, p, p, None, None, 0, None) == ta.TA_ERR_INVALID_ARG
+    assert L.tree_attn_prefill(h, bf, 2, 1, 32, 0.2, fa.odd, p, p, p, None, None, 0, None) == ta.TA_ERR_INVALID_ARG
     # wrong plan kind for the entry point
-    assert L.tree_attn_verify(h, bf, 2, 1, 32, 0.2, p, p, p, p, p, p, None, None) == ta.TA_ERR_STATE
+    assert L.tree_attn_verify(h, bf, 2, 1, 32, 0.2, p, p, p, p, p, p, None, None, 0, None) == ta.TA_ERR_STATE
     # workspace checks of upload happen before any copy
     assert L.tree_attn_plan_upload(h, None, 1 << 20, None) == ta.TA_ERR_WORKSPACE
     assert L.tree_attn_plan_upload(h, fa.odd, 1 << 20, None) == ta.TA_ERR_INVALID_ARG
@@ -178,7 +178,7 @@ def test_decode_scratch_errors():
     fa = FakeArgs()
     p = fa.p
     plan = ta.plan_decode([10], [2], [1, 1], [0, 0], [1, 2], [3, 0])
-    need = ta.decode_scratch_bytes(plan, 4, 32)
+    need = ta.scratch_bytes(plan, 4, 32)
     assert need > 0
     bf = ta.TA_DTYPE_BF16
     rc = L.tree_attn_decode(plan.handle, bf, 4, 2, 32, 0.2, p, p, p, p, p, p, None, None, need, None)
@@ -194,3 +194,70 @@ def test_export_errors():
     with pytest.raises(ta.TreeAttnError) as e:
         ta.plan_export(plan, "verify_mask")
     assert e.value.code == ta.TA_ERR_INVALID_ARG
+
+
+# --------------------------------------------------------------------------
+# load balancing by key-range splits
+# --------------------------------------------------------------------------
+
+def _pieces_cover(plan, desc_rows):
+    """Every row tile's key tiles are covered exactly once by its pieces, and
+    split pieces own disjoint partial slots that the merge table lists."""
+    work = plan.export("work")
+    by_tile = {}
+    for w in work:
+        by_tile.setdefault((int(w[0]), int(w[1])), []).append(w)
+    rows_split = 0
+    slots = set()
+    for (row0, nrows), pieces in by_tile.items():
+        pieces.sort(key=lambda w: w[8])
+        assert pieces[0][8] == 0
+        for a, b in zip(pieces, pieces[1:]):
+            assert a[9] == b[8]
+        na = (pieces[0][4] - pieces[0][2] + 63) // 64
+        nb = (pieces[0][6] - pieces[0][5] + 63) // 64
+        assert pieces[-1][9] == na + nb
+        if len(pieces) > 1:
+            rows_split += nrows
+            for w in pieces:
+                assert w[7] >= 0
+                for t in range(nrows):
+                    assert w[7] + t not in slots
+                    slots.add(int(w[7] + t))
+        else:
+            assert pieces[0][7] == -1
+    return rows_split, len(slots)
+
+
+def test_balance_splits_the_one_page_prefill():
+    w = synth.config2(with_tensors=False)
+    plan = ta.plan_for(w.desc)
+    before = plan.export("work").shape[0]
+    plan.balance(8, 512)
+    info = plan.info
+    assert plan.export("work").shape[0] > before
+    rows_split, n_slots = _pieces_cover(plan, w.desc.total_tokens())
+    assert rows_split > 0 and info["n_partials"] == n_slots
+    assert ta.scratch_bytes(plan, 16, 128) > 0
+    # the integer contract is unchanged by balancing
+    ref = oracle.plan_prefill(w.desc)
+    assert np.array_equal(plan.export("main_end"), ref["main_end"])
+
+
+def test_balance_leaves_balanced_plans_alone():
+    w = synth.config3(with_tensors=False)
+    plan = ta.plan_for(w.desc)
+    before = plan.export("work")
+    plan.balance(8, 512)
+    assert plan.info["n_partials"] == 0
+    assert np.array_equal(plan.export("work"), before)
+
+
+def test_balance_errors():
+    plan = ta.plan_for(synth.config2(with_tensors=False).desc)
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_balance, plan, 0, 512)
+    plan.balance(8, 512)
+    assert plan.info["n_partials"] > 0
+    expect(ta.TA_ERR_STATE, ta.plan_balance, plan, 8, 512)
+    d = ta.plan_decode([10], [1], [1], [0], [1], [3])
+    d.balance(8, 512)           # no-op for decode

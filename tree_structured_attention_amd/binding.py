@@ -6,9 +6,9 @@ device workspace/scratch with torch, and raises on a non-zero status.  It
 fails loudly if the library has not been built: there is no fallback.
 
 Names mirror the C entry points without the ``tree_attn_`` prefix:
-``plan_prefill``, ``plan_decode``, ``plan_verify``, ``plan_info``,
-``plan_export``, ``plan_upload``, ``plan_destroy``, ``decode_scratch_bytes``,
-``prefill``, ``decode``, ``verify``.
+``plan_prefill``, ``plan_decode``, ``plan_verify``, ``plan_balance``,
+``plan_info``, ``plan_export``, ``plan_upload``, ``plan_destroy``,
+``scratch_bytes``, ``prefill``, ``decode``, ``verify``.
 """
 from __future__ import annotations
 
@@ -50,7 +50,7 @@ FIELD = {
     "verify_rows": 8,
     "work": 9,
 }
-FIELD_WIDTH = {"pages": 5, "branches": 3, "decode_rows": 5, "verify_rows": 4, "work": 8}
+FIELD_WIDTH = {"pages": 5, "branches": 3, "decode_rows": 5, "verify_rows": 4, "work": 10}
 
 
 class TreeAttnError(RuntimeError):
@@ -102,11 +102,13 @@ def lib() -> ctypes.CDLL:
             "tree_attn_plan_export": ([_P, i32, ctypes.POINTER(i64), i64, ctypes.POINTER(i64)], ctypes.c_int),
             "tree_attn_plan_upload": ([_P, _P, sz, _P], ctypes.c_int),
             "tree_attn_plan_destroy": ([_P], None),
-            "tree_attn_decode_scratch_bytes": ([_P, i32, i32, ctypes.POINTER(sz)], ctypes.c_int),
-            "tree_attn_prefill": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+            "tree_attn_plan_balance": ([_P, i32, i32], ctypes.c_int),
+            "tree_attn_scratch_bytes": ([_P, i32, i32, ctypes.POINTER(sz)], ctypes.c_int),
+            "tree_attn_prefill": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P, sz, _P], ctypes.c_int),
             "tree_attn_decode": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
                                  ctypes.c_int),
-            "tree_attn_verify": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+            "tree_attn_verify": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
+                                 ctypes.c_int),
             "tree_attn_last_error": ([], ctypes.c_char_p),
             "tree_attn_version": ([], ctypes.c_char_p),
         }
@@ -165,6 +167,9 @@ class Plan:
     def upload(self, device=None, stream=None) -> "Plan":
         return plan_upload(self, device, stream)
 
+    def balance(self, n_kv_heads: int, n_slots: int = None) -> "Plan":
+        return plan_balance(self, n_kv_heads, n_slots)
+
     def close(self):
         if self.handle is not None and self.handle.value:
             lib().tree_attn_plan_destroy(self.handle)
@@ -214,6 +219,20 @@ def plan_for(desc) -> Plan:
     raise TypeError(f"no plan for {name}")
 
 
+def default_slots() -> int:
+    """Concurrent workgroups of the attention kernel on the current GPU
+    (2 per compute unit; 512 on MI355X)."""
+    try:
+        return 2 * torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    except Exception:
+        return 512
+
+
+def plan_balance(plan: Plan, n_kv_heads: int, n_slots: int = None) -> Plan:
+    _check(lib().tree_attn_plan_balance(plan.handle, int(n_kv_heads), int(n_slots or default_slots())))
+    return plan
+
+
 def plan_info(plan: Plan) -> dict:
     info = PlanInfo()
     _check(lib().tree_attn_plan_info(plan.handle, ctypes.byref(info)))
@@ -256,10 +275,22 @@ def plan_destroy(plan: Plan):
     plan.close()
 
 
-def decode_scratch_bytes(plan: Plan, hq: int, head_dim: int) -> int:
+def scratch_bytes(plan: Plan, hq: int, head_dim: int) -> int:
     n = ctypes.c_size_t()
-    _check(lib().tree_attn_decode_scratch_bytes(plan.handle, hq, head_dim, ctypes.byref(n)))
+    _check(lib().tree_attn_scratch_bytes(plan.handle, hq, head_dim, ctypes.byref(n)))
     return int(n.value)
+
+
+def _scratch(plan, hq, d, device, scratch):
+    """Caller-provided scratch (uint8 tensor) or a fresh one; 256-byte aligned view."""
+    need = scratch_bytes(plan, hq, d)
+    if need == 0:
+        return None, 0
+    if scratch is None:
+        scratch = torch.empty(need + 256, dtype=torch.uint8, device=device)
+    off = (-scratch.data_ptr()) % 256
+    view = scratch[off:]
+    return ctypes.c_void_p(view.data_ptr()), view.numel()
 
 
 # ---------------------------------------------------------------------------
@@ -302,11 +333,14 @@ def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def prefill(plan: Plan, q, k, v, scale=None, want_lse=True, out=None, lse=None, stream=None):
+def prefill(plan: Plan, q, k, v, scale=None, want_lse=True, out=None, lse=None,
+            scratch: Optional[torch.Tensor] = None, stream=None):
     hq, hkv, d = _heads(q, k)
     o, l = _outputs(q, want_lse, out, lse)
+    sp, sn = _scratch(plan, hq, d, q.device, scratch)
     _check(lib().tree_attn_prefill(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
-                                   _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(l), _stream_handle(stream)))
+                                   _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(l), sp, sn,
+                                   _stream_handle(stream)))
     return o, l
 
 
@@ -314,23 +348,19 @@ def decode(plan: Plan, q, k_main, v_main, k_suffix, v_suffix, scale=None, want_l
            scratch: Optional[torch.Tensor] = None, stream=None):
     hq, hkv, d = _heads(q, k_main)
     o, l = _outputs(q, want_lse, out, lse)
-    need = decode_scratch_bytes(plan, hq, d)
-    if scratch is None:
-        scratch = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
-    off = (-scratch.data_ptr()) % 256
-    sview = scratch[off:]
+    sp, sn = _scratch(plan, hq, d, q.device, scratch)
     _check(lib().tree_attn_decode(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
                                   _dev_ptr(k_main), _dev_ptr(v_main), _dev_ptr(k_suffix), _dev_ptr(v_suffix),
-                                  _dev_ptr(o), _dev_ptr(l), ctypes.c_void_p(sview.data_ptr()), sview.numel(),
-                                  _stream_handle(stream)))
+                                  _dev_ptr(o), _dev_ptr(l), sp, sn, _stream_handle(stream)))
     return o, l
 
 
 def verify(plan: Plan, q, k_ctx, v_ctx, k_tree, v_tree, scale=None, want_lse=True, out=None, lse=None,
-           stream=None):
+           scratch: Optional[torch.Tensor] = None, stream=None):
     hq, hkv, d = _heads(q, k_ctx)
     o, l = _outputs(q, want_lse, out, lse)
+    sp, sn = _scratch(plan, hq, d, q.device, scratch)
     _check(lib().tree_attn_verify(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
                                   _dev_ptr(k_ctx), _dev_ptr(v_ctx), _dev_ptr(k_tree), _dev_ptr(v_tree),
-                                  _dev_ptr(o), _dev_ptr(l), _stream_handle(stream)))
+                                  _dev_ptr(o), _dev_ptr(l), sp, sn, _stream_handle(stream)))
     return o, l

@@ -75,9 +75,39 @@ int hip_status(hipError_t e, const char* who) {
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
-int64_t decode_scratch(const ta_plan* plan, int32_t hq, int32_t d) {
+int64_t scratch_need(const ta_plan* plan, int32_t hq, int32_t d) {
   const int64_t slots = plan->n_partials * hq;
+  if (slots == 0) return 0;
   return align256(slots * d * 4) + align256(slots * 2 * 4);
+}
+
+int check_scratch(const ta_plan* plan, int32_t hq, int32_t d, void* scratch, size_t bytes, const char* who) {
+  const int64_t need = scratch_need(plan, hq, d);
+  if (need == 0) return TA_OK;
+  if (!scratch) return fail(TA_ERR_WORKSPACE, std::string(who) + ": scratch is NULL (tree_attn_scratch_bytes > 0)");
+  if (!aligned(scratch, 256)) return fail(TA_ERR_INVALID_ARG, std::string(who) + ": scratch must be 256-byte aligned");
+  if (int64_t(bytes) < need) return fail(TA_ERR_WORKSPACE, std::string(who) + ": scratch smaller than tree_attn_scratch_bytes");
+  return TA_OK;
+}
+
+void set_partials(AttnParams& p, const ta_plan* plan, int32_t hq, int32_t d, void* scratch) {
+  const int64_t slots = plan->n_partials * hq;
+  p.part_acc = static_cast<float*>(scratch);
+  p.part_ml = slots ? reinterpret_cast<float*>(static_cast<unsigned char*>(scratch) + align256(slots * d * 4)) : nullptr;
+}
+
+hipError_t launch_merge_for(const ta_plan* plan, int dtype, const AttnParams& p, int32_t d, hipStream_t st) {
+  if (plan->merge.empty()) return hipSuccess;
+  MergeParams m{};
+  m.merge = reinterpret_cast<const MergeRow*>(static_cast<const unsigned char*>(plan->dev) + plan->layout.merge);
+  m.part_acc = p.part_acc;
+  m.part_ml = p.part_ml;
+  m.o = p.o;
+  m.lse = p.lse;
+  m.n_rows = int32_t(plan->n_rows);
+  m.n_merge = int32_t(plan->merge.size());
+  m.hq = p.hq;
+  return launch_merge(dtype, m, d, st);
 }
 
 }  // namespace
@@ -122,7 +152,8 @@ extern "C" int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t
     case TA_FIELD_VERIFY_ROWS: if (k == TA_PLAN_VERIFY) src = &plan->verify_rows4; break;
     case TA_FIELD_WORK:
       for (const WorkItem& w : plan->work)
-        work_tmp.insert(work_tmp.end(), {w.row0, w.nrows, w.a_lo, w.a_full, w.a_hi, w.b_lo, w.b_hi, w.out});
+        work_tmp.insert(work_tmp.end(), {w.row0, w.nrows, w.a_lo, w.a_full, w.a_hi, w.b_lo, w.b_hi, w.out,
+                                         w.tile_lo, w.tile_hi});
       src = &work_tmp;
       break;
     default: break;
@@ -167,17 +198,16 @@ extern "C" void tree_attn_plan_destroy(ta_plan* plan) {
   delete plan;
 }
 
-extern "C" int tree_attn_decode_scratch_bytes(const ta_plan* plan, int32_t hq, int32_t head_dim, size_t* bytes) {
-  if (!plan || !bytes) return fail(TA_ERR_INVALID_ARG, "decode_scratch_bytes: NULL argument");
-  if (plan->kind != TA_PLAN_DECODE) return fail(TA_ERR_STATE, "decode_scratch_bytes: not a decode plan");
-  if (hq <= 0 || head_dim <= 0) return fail(TA_ERR_INVALID_ARG, "decode_scratch_bytes: hq and head_dim must be positive");
-  *bytes = size_t(decode_scratch(plan, hq, head_dim));
+extern "C" int tree_attn_scratch_bytes(const ta_plan* plan, int32_t hq, int32_t head_dim, size_t* bytes) {
+  if (!plan || !bytes) return fail(TA_ERR_INVALID_ARG, "scratch_bytes: NULL argument");
+  if (hq <= 0 || head_dim <= 0) return fail(TA_ERR_INVALID_ARG, "scratch_bytes: hq and head_dim must be positive");
+  *bytes = size_t(scratch_need(plan, hq, head_dim));
   return TA_OK;
 }
 
 extern "C" int tree_attn_prefill(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim,
                                  float scale, const void* q, const void* k, const void* v, void* o, float* lse,
-                                 void* stream) {
+                                 void* scratch, size_t scratch_bytes, void* stream) {
   int rc = check_plan(plan, TA_PLAN_PREFILL, "prefill");
   if (rc) return rc;
   if ((rc = check_heads(dtype, hq, hkv, head_dim, scale))) return rc;
@@ -186,6 +216,7 @@ extern "C" int tree_attn_prefill(const ta_plan* plan, int32_t dtype, int32_t hq,
       (rc = check_tensor(o, rows, "o")))
     return rc;
   if (lse && !aligned(lse, 4)) return fail(TA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if ((rc = check_scratch(plan, hq, head_dim, scratch, scratch_bytes, "prefill"))) return rc;
   if ((rc = check_uploaded(plan, "prefill"))) return rc;
   AttnParams p = base_params(plan, hq, hkv, scale);
   p.q = q;
@@ -193,13 +224,17 @@ extern "C" int tree_attn_prefill(const ta_plan* plan, int32_t dtype, int32_t hq,
   p.va = p.vb = v;
   p.o = o;
   p.lse = lse;
-  return hip_status(launch_attention(kPrefill, dtype, p, int(plan->work.size()), head_dim, static_cast<hipStream_t>(stream)),
-                    "prefill launch");
+  set_partials(p, plan, hq, head_dim, scratch);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = hip_status(launch_attention(kPrefill, dtype, p, int(plan->work.size()), head_dim, st), "prefill launch");
+  if (rc) return rc;
+  return hip_status(launch_merge_for(plan, dtype, p, head_dim, st), "prefill merge launch");
 }
 
 extern "C" int tree_attn_verify(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim,
                                 float scale, const void* q, const void* k_ctx, const void* v_ctx, const void* k_tree,
-                                const void* v_tree, void* o, float* lse, void* stream) {
+                                const void* v_tree, void* o, float* lse, void* scratch, size_t scratch_bytes,
+                                void* stream) {
   int rc = check_plan(plan, TA_PLAN_VERIFY, "verify");
   if (rc) return rc;
   if ((rc = check_heads(dtype, hq, hkv, head_dim, scale))) return rc;
@@ -209,6 +244,7 @@ extern "C" int tree_attn_verify(const ta_plan* plan, int32_t dtype, int32_t hq, 
       (rc = check_tensor(v_tree, rows, "v_tree")) || (rc = check_tensor(o, rows, "o")))
     return rc;
   if (lse && !aligned(lse, 4)) return fail(TA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if ((rc = check_scratch(plan, hq, head_dim, scratch, scratch_bytes, "verify"))) return rc;
   if ((rc = check_uploaded(plan, "verify"))) return rc;
   AttnParams p = base_params(plan, hq, hkv, scale);
   p.q = q;
@@ -218,8 +254,11 @@ extern "C" int tree_attn_verify(const ta_plan* plan, int32_t dtype, int32_t hq, 
   p.vb = v_tree;
   p.o = o;
   p.lse = lse;
-  return hip_status(launch_attention(kVerify, dtype, p, int(plan->work.size()), head_dim, static_cast<hipStream_t>(stream)),
-                    "verify launch");
+  set_partials(p, plan, hq, head_dim, scratch);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = hip_status(launch_attention(kVerify, dtype, p, int(plan->work.size()), head_dim, st), "verify launch");
+  if (rc) return rc;
+  return hip_status(launch_merge_for(plan, dtype, p, head_dim, st), "verify merge launch");
 }
 
 extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim,
@@ -235,12 +274,7 @@ extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, 
       (rc = check_tensor(v_suffix, plan->n_keys_b, "v_suffix")) || (rc = check_tensor(o, rows, "o")))
     return rc;
   if (lse && !aligned(lse, 4)) return fail(TA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  const int64_t need = decode_scratch(plan, hq, head_dim);
-  if (rows > 0) {
-    if (!scratch) return fail(TA_ERR_WORKSPACE, "decode: scratch is NULL");
-    if (!aligned(scratch, 256)) return fail(TA_ERR_INVALID_ARG, "decode: scratch must be 256-byte aligned");
-    if (int64_t(scratch_bytes) < need) return fail(TA_ERR_WORKSPACE, "decode: scratch smaller than tree_attn_decode_scratch_bytes");
-  }
+  if ((rc = check_scratch(plan, hq, head_dim, scratch, scratch_bytes, "decode"))) return rc;
   if ((rc = check_uploaded(plan, "decode"))) return rc;
   AttnParams p = base_params(plan, hq, hkv, scale);
   p.q = q;
@@ -250,19 +284,9 @@ extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, 
   p.vb = v_suffix;
   p.o = o;
   p.lse = lse;
-  const int64_t slots = plan->n_partials * hq;
-  p.part_acc = static_cast<float*>(scratch);
-  p.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(scratch) + align256(slots * head_dim * 4));
+  set_partials(p, plan, hq, head_dim, scratch);
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = hip_status(launch_attention(kDecode, dtype, p, int(plan->work.size()), head_dim, st), "decode launch");
   if (rc) return rc;
-  MergeParams m{};
-  m.merge = reinterpret_cast<const MergeRow*>(static_cast<const unsigned char*>(plan->dev) + plan->layout.merge);
-  m.part_acc = p.part_acc;
-  m.part_ml = p.part_ml;
-  m.o = o;
-  m.lse = lse;
-  m.n_rows = int32_t(rows);
-  m.hq = hq;
-  return hip_status(launch_merge(dtype, m, head_dim, st), "decode merge launch");
+  return hip_status(launch_merge_for(plan, dtype, p, head_dim, st), "decode merge launch");
 }

@@ -358,11 +358,14 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
 
   TileLoader<T, D, NW> loader;
   loader.init(lane, wave, kv_stride);
-  if (n_tiles > 0) {
-    if (n_a > 0)
-      loader.issue(lds, ka, va, wi.a_lo, wi.a_hi, kv_stride, wave);
+  // this item's tiles: [tile_lo, tile_hi) of segment A's tiles then B's
+  const int it_lo = wi.tile_lo, it_hi = min(wi.tile_hi, n_tiles);
+  if (it_lo < it_hi) {
+    unsigned char* stage = lds + (it_lo & 1) * G::kStageBytes;
+    if (it_lo < n_a)
+      loader.issue(stage, ka, va, wi.a_lo + it_lo * kKeyTile, wi.a_hi, kv_stride, wave);
     else
-      loader.issue(lds, kb, vb, wi.b_lo, wi.b_hi, kv_stride, wave);
+      loader.issue(stage, kb, vb, wi.b_lo + (it_lo - n_a) * kKeyTile, wi.b_hi, kv_stride, wave);
   }
 
   RS rs;
@@ -407,18 +410,19 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
     for (int i = 0; i < 16; ++i) rs.acc[md][i] = 0.f;
   const bool wave_active = wave * TPW < wi.nrows;
 
-  // Four runs: seg A unmasked, seg A masked, seg B unmasked, seg B masked.
-  int it = 0;
+  // Four runs: seg A unmasked, seg A masked, seg B unmasked, seg B masked,
+  // each clipped to this item's tile range.
+  int it = it_lo;
 #pragma unroll 1
   for (int run = 0; run < 4; ++run) {
     const bool seg_a = run < 2;
-    const int run_end = run == 0 ? fa : run == 1 ? n_a : run == 2 ? n_a + fb : n_tiles;
+    const int run_end = min(it_hi, run == 0 ? fa : run == 1 ? n_a : run == 2 ? n_a + fb : n_tiles);
     const int t_hi = seg_a ? wi.a_hi : wi.b_hi;
 #pragma unroll 1
     for (; it < run_end; ++it) {
       const int t0 = seg_a ? wi.a_lo + it * kKeyTile : wi.b_lo + (it - n_a) * kKeyTile;
       __syncthreads();  // tile `it` has landed; every wave is done with tile it-1
-      if (it + 1 < n_tiles) {
+      if (it + 1 < it_hi) {
         const int nx = it + 1;
         unsigned char* stage = lds + (nx & 1) * G::kStageBytes;
         if (nx < n_a)
@@ -436,7 +440,7 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   const float l_tot = pair_sum(rs.l_run);
   if (!rs.row_ok) return;
   const int h = rs.h;
-  if constexpr (MODE == kDecode) {
+  if (MODE == kDecode || wi.out >= 0) {
     const int64_t slot = int64_t(wi.out) + tok;
     const int64_t idx = slot * p.hq + head;
     float* dst = p.part_acc + idx * D;
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// decode merge: one (branch, query head) per 64-lane group, fixed order
+// merge of fp32 partials: one (row, query head) per 64-lane group, fixed order
 // ---------------------------------------------------------------------------
 
 template <typename T, int D>
@@ -484,9 +488,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   constexpr int kPer = D / 64 > 0 ? D / 64 : 1;  // dims per lane
   const int lane = threadIdx.x & 63;
   const int64_t pair = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (pair >= int64_t(p.n_rows) * p.hq) return;
-  const int row = int(pair / p.hq), head = int(pair % p.hq);
-  const MergeRow mr = p.merge[row];
+  if (pair >= int64_t(p.n_merge) * p.hq) return;
+  const MergeRow mr = p.merge[pair / p.hq];
+  const int row = mr.row, head = int(pair % p.hq);
   float mx = -INFINITY;
   for (int c = 0; c < mr.sh_count; ++c)
     mx = fmaxf(mx, p.part_ml[(int64_t(mr.sh_first + c * mr.sh_stride) * p.hq + head) * 2]);
@@ -577,7 +581,7 @@ hipError_t launch_attention(int mode, int dtype, const AttnParams& p, int n_work
 }
 
 hipError_t launch_merge(int dtype, const MergeParams& p, int d, hipStream_t st) {
-  const int64_t pairs = int64_t(p.n_rows) * p.hq;
+  const int64_t pairs = int64_t(p.n_merge) * p.hq;
   if (pairs == 0) return hipSuccess;
   dim3 grid(unsigned((pairs + 3) / 4));
   if (dtype == TA_DTYPE_BF16) {

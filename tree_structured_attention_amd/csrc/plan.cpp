@@ -29,7 +29,8 @@ constexpr int64_t kMax32 = INT32_MAX;
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 int64_t item_cost(const WorkItem& w) {
-  return int64_t(w.nrows) * (int64_t(w.a_hi - w.a_lo) + int64_t(w.b_hi - w.b_lo) + 16);
+  const int64_t tiles = w.tile_hi - w.tile_lo;
+  return int64_t(w.nrows) * (tiles * kKeyTile + 16);
 }
 
 // Longest first, so that the long tiles start early and the short ones fill
@@ -51,10 +52,16 @@ WorkItem make_item(int64_t row0, int64_t nrows, int64_t a_lo, int64_t a_full, in
   w.b_hi = int32_t(std::max(b_lo, b_hi));
   w.out = int32_t(out);
   w.flags = flags;
+  w.tile_lo = 0;
+  w.tile_hi = int32_t(item_tiles(w));
   return w;
 }
 
 }  // namespace
+
+int64_t item_tiles(const WorkItem& w) {
+  return (int64_t(w.a_hi - w.a_lo) + kKeyTile - 1) / kKeyTile + (int64_t(w.b_hi - w.b_lo) + kKeyTile - 1) / kKeyTile;
+}
 
 void pack_blob(ta_plan* p) {
   DeviceLayout L;
@@ -286,6 +293,7 @@ extern "C" int tree_attn_plan_decode(const int32_t* prefix_len, const int32_t* n
       }
       for (int32_t i = g0; i < g1; ++i) {
         MergeRow& mr = pl->merge[i];
+        mr.row = i;
         mr.sh_first = int32_t(first + (i - g0));
         mr.sh_count = int32_t((main_len[i] + kDecodeChunk - 1) / kDecodeChunk);
         mr.sh_stride = g1 - g0;
@@ -400,5 +408,106 @@ extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, co
   order_work(pl->work);
   pack_blob(pl);
   *out = pl;
+  return TA_OK;
+}
+
+namespace {
+
+// Makespan of dispatching `jobs` (costs, in dispatch order, each once per KV
+// head with the heads adjacent) to `slots` identical workgroup slots, each
+// job going to the slot that frees first.
+int64_t simulate_makespan(const std::vector<int64_t>& jobs, int hkv, int slots) {
+  std::vector<int64_t> heap(size_t(slots), 0);  // min-heap of slot finish times
+  auto cmp = [](int64_t a, int64_t b) { return a > b; };
+  for (int64_t c : jobs)
+    for (int k = 0; k < hkv; ++k) {
+      std::pop_heap(heap.begin(), heap.end(), cmp);
+      heap.back() += c;
+      std::push_heap(heap.begin(), heap.end(), cmp);
+    }
+  return *std::max_element(heap.begin(), heap.end());
+}
+
+constexpr int64_t kItemOverhead = 3;  // prologue/epilogue of a workgroup, in tiles
+
+}  // namespace
+
+extern "C" int tree_attn_plan_balance(ta_plan* plan, int32_t n_kv_heads, int32_t n_slots) {
+  if (!plan) return fail(TA_ERR_INVALID_ARG, "plan_balance: plan is NULL");
+  if (n_kv_heads <= 0 || n_slots <= 0) return fail(TA_ERR_INVALID_ARG, "plan_balance: counts must be positive");
+  if (plan->kind == TA_PLAN_DECODE) return TA_OK;  // decode items are already key chunks
+  if (plan->dev) return fail(TA_ERR_STATE, "plan_balance: plan already uploaded");
+  if (plan->n_partials > 0) return fail(TA_ERR_STATE, "plan_balance: plan already balanced");
+  // pieces as (item, tile_lo, tile_hi)
+  struct Piece { int32_t item, lo, hi; };
+  std::vector<WorkItem>& work = plan->work;
+  std::vector<Piece> pieces;
+  int64_t total = 0;
+  for (int32_t i = 0; i < int32_t(work.size()); ++i) {
+    pieces.push_back({i, 0, work[i].tile_hi});
+    total += work[i].tile_hi + kItemOverhead;
+  }
+  auto cost = [](const Piece& p) { return int64_t(p.hi - p.lo) + kItemOverhead; };
+  auto order = [&](std::vector<Piece>& v) {
+    std::stable_sort(v.begin(), v.end(), [&](const Piece& a, const Piece& b) { return cost(a) > cost(b); });
+  };
+  const double balanced = double(total) * n_kv_heads / n_slots;
+  for (int iter = 0; iter < 1024 && !pieces.empty(); ++iter) {
+    order(pieces);
+    std::vector<int64_t> jobs;
+    for (const Piece& p : pieces) jobs.push_back(cost(p));
+    const int64_t mk = simulate_makespan(jobs, n_kv_heads, n_slots);
+    if (double(mk) <= 1.08 * balanced + kItemOverhead) break;
+    Piece& big = pieces.front();
+    if (big.hi - big.lo < 4) break;  // not worth splitting further
+    const int32_t mid = big.lo + (big.hi - big.lo) / 2;
+    Piece tail{big.item, mid, big.hi};
+    big.hi = mid;
+    pieces.push_back(tail);
+  }
+  // Rebuild the work list: unsplit items stay direct; the pieces of a split
+  // item get consecutive partial slots (piece p, row t -> base + p*nrows + t).
+  std::vector<int32_t> n_pieces(work.size(), 0);
+  for (const Piece& p : pieces) n_pieces[p.item]++;
+  std::sort(pieces.begin(), pieces.end(),
+            [](const Piece& a, const Piece& b) { return a.item != b.item ? a.item < b.item : a.lo < b.lo; });
+  std::vector<WorkItem> out;
+  std::vector<MergeRow> merge;
+  int64_t slot = 0;
+  size_t k = 0;
+  while (k < pieces.size()) {
+    const int32_t item = pieces[k].item;
+    const WorkItem& w = work[item];
+    if (n_pieces[item] == 1) {
+      out.push_back(w);
+      ++k;
+      continue;
+    }
+    const int64_t base = slot;
+    for (int32_t pc = 0; pc < n_pieces[item]; ++pc, ++k) {
+      WorkItem piece = w;
+      piece.tile_lo = pieces[k].lo;
+      piece.tile_hi = pieces[k].hi;
+      piece.out = int32_t(base + int64_t(pc) * w.nrows);
+      out.push_back(piece);
+    }
+    for (int32_t t = 0; t < w.nrows; ++t) {
+      MergeRow mr{};
+      mr.sh_first = int32_t(base + t);
+      mr.sh_count = n_pieces[item];
+      mr.sh_stride = w.nrows;
+      mr.sf_first = 0;
+      mr.sf_count = 0;
+      mr.row = w.row0 + t;
+      merge.push_back(mr);
+    }
+    slot += int64_t(n_pieces[item]) * w.nrows;
+    if (slot >= kMax32) return fail(TA_ERR_CAPACITY, "plan_balance: partial slots >= 2^31");
+  }
+  order_work(out);
+  plan->work.swap(out);
+  plan->merge.swap(merge);
+  plan->n_partials = slot;
+  pack_blob(plan);
   return TA_OK;
 }

@@ -26,19 +26,25 @@ constexpr int kDecodeSuffixWhole = 2048;
 //         tile; keys in [a_full, a_hi) are tested per row against row_a.
 //   seg B [b_lo, b_hi): always tested per row (prefill: branch-causal;
 //         verify: tree bitmask; decode suffix: visible, flag kSegBFull).
-//   out   decode: first partial slot of the tile (per query head); else -1.
+//   out   first partial slot of the tile (per query head) when the item
+//         writes fp32 partials (decode; split prefill/verify pieces); else -1.
 //   flags bit 0: seg B fully visible.
+//   [tile_lo, tile_hi) the 64-key tiles (segment A's, then segment B's) this
+//         item walks; a prefill/verify row tile split for load balance has
+//         one item per piece.
 struct WorkItem {
   int32_t row0, nrows, a_lo, a_full, a_hi, b_lo, b_hi, out;
-  int32_t flags, pad0, pad1, pad2;
+  int32_t flags, tile_lo, tile_hi, pad0;
 };
 static_assert(sizeof(WorkItem) == 48, "work item layout");
 constexpr int32_t kSegBFull = 1;
 
-// Decode merge table, one entry per live branch: shared partial slots are
-// sh_first + c * sh_stride (c < sh_count), suffix slots sf_first + c.
+// Merge table, one entry per output row combined from partials: slots are
+// sh_first + c * sh_stride (c < sh_count), then sf_first + c (c < sf_count),
+// merged in that order.  Decode: every branch (main-stream chunks, then its
+// suffix chunks).  Prefill/verify: the rows of split row tiles.
 struct MergeRow {
-  int32_t sh_first, sh_count, sh_stride, sf_first, sf_count, pad0, pad1, pad2;
+  int32_t sh_first, sh_count, sh_stride, sf_first, sf_count, row, pad0, pad1;
 };
 static_assert(sizeof(MergeRow) == 32, "merge row layout");
 
@@ -78,6 +84,7 @@ struct ta_plan {
 };
 
 namespace ta {
+int64_t item_tiles(const WorkItem& w);
 void set_error(const std::string& msg);
 int fail(int code, const std::string& msg);
 void pack_blob(ta_plan* p);

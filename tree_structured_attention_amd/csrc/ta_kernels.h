@@ -31,12 +31,14 @@ struct AttnParams {
 };
 
 struct MergeParams {
-  const MergeRow* merge;
+  const MergeRow* merge;  // n_merge entries
   const float* part_acc;
   const float* part_ml;
   void* o;
   float* lse;
-  int32_t n_rows, hq;
+  int32_t n_rows;   // rows of o / lse (lse is [hq, n_rows])
+  int32_t n_merge;  // merge-table entries
+  int32_t hq;
 };
 
 hipError_t launch_attention(int mode, int dtype, const AttnParams& p, int n_work, int head_dim, hipStream_t st);
