@@ -336,7 +336,8 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   constexpr int kQSteps = RS::kQSteps;
   constexpr int kDB = RS::kDB;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * G::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[G::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[G::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   // this item's tiles: [tile_lo, tile_hi) of segment A's tiles then B's
   const int it_lo = wi.tile_lo, it_hi = min(wi.tile_hi, n_tiles);
   if (it_lo < it_hi) {
-    unsigned char* stage = lds + (it_lo & 1) * G::kStageBytes;
+    unsigned char* stage = lds0;
     if (it_lo < n_a)
       loader.issue(stage, ka, va, wi.a_lo + it_lo * kKeyTile, wi.a_hi, kv_stride, wave);
     else
@@ -410,30 +411,34 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
     for (int i = 0; i < 16; ++i) rs.acc[md][i] = 0.f;
   const bool wave_active = wave * TPW < wi.nrows;
 
-  // Four runs: seg A unmasked, seg A masked, seg B unmasked, seg B masked,
-  // each clipped to this item's tile range.
-  int it = it_lo;
-#pragma unroll 1
-  for (int run = 0; run < 4; ++run) {
-    const bool seg_a = run < 2;
-    const int run_end = min(it_hi, run == 0 ? fa : run == 1 ? n_a : run == 2 ? n_a + fb : n_tiles);
-    const int t_hi = seg_a ? wi.a_hi : wi.b_hi;
-#pragma unroll 1
-    for (; it < run_end; ++it) {
-      const int t0 = seg_a ? wi.a_lo + it * kKeyTile : wi.b_lo + (it - n_a) * kKeyTile;
-      __syncthreads();  // tile `it` has landed; every wave is done with tile it-1
-      if (it + 1 < it_hi) {
-        const int nx = it + 1;
-        unsigned char* stage = lds + (nx & 1) * G::kStageBytes;
-        if (nx < n_a)
-          loader.issue(stage, ka, va, wi.a_lo + nx * kKeyTile, wi.a_hi, kv_stride, wave);
-        else
-          loader.issue(stage, kb, vb, wi.b_lo + (nx - n_a) * kKeyTile, wi.b_hi, kv_stride, wave);
-      }
-      if (!wave_active) continue;
-      const unsigned char* kl = lds + (it & 1) * G::kStageBytes;
-      rs.consume(kl, kl + G::kTileBytes, t0, t_hi, seg_a, (run & 1) != 0);
+  // Tiles alternate between two LDS buffers, so each is a distinct object:
+  // the next tile's copy into one never has to complete before reads of the
+  // other.
+  const int a_lo = wi.a_lo, a_hi = wi.a_hi, b_lo = wi.b_lo, b_hi = wi.b_hi;
+  auto step = [&](int it, const unsigned char* cur, unsigned char* nxt) {
+    // this wave's copies into `cur` are done (vmcnt(0)), then the barrier
+    // publishes all of them and retires every wave's reads of `nxt`
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (it + 1 < it_hi) {
+      const int nx = it + 1;
+      if (nx < n_a)
+        loader.issue(nxt, ka, va, a_lo + nx * kKeyTile, a_hi, kv_stride, wave);
+      else
+        loader.issue(nxt, kb, vb, b_lo + (nx - n_a) * kKeyTile, b_hi, kv_stride, wave);
     }
+    if (wave_active) {
+      const bool seg_a = it < n_a;
+      const int t0 = seg_a ? a_lo + it * kKeyTile : b_lo + (it - n_a) * kKeyTile;
+      const int t_hi = seg_a ? a_hi : b_hi;
+      const bool masked = seg_a ? it >= fa : (it - n_a) >= fb;
+      rs.consume(cur, cur + G::kTileBytes, t0, t_hi, seg_a, masked);
+    }
+  };
+#pragma unroll 1
+  for (int it = it_lo; it < it_hi; it += 2) {
+    step(it, lds0, lds1);
+    if (it + 1 < it_hi) step(it + 1, lds1, lds0);
   }
 
   // ---- epilogue ----
