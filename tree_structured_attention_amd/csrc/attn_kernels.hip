@@ -158,6 +158,18 @@ struct TileLoader {
   }
 };
 
+// Scheduling groups: AHEAD LDS reads up front, then per matrix instruction
+// one MFMA and the PER reads of a later one.
+template <int I, int NM, int PER, int AHEAD>
+__device__ __forceinline__ void sched_ld_mfma() {
+  if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (AHEAD + (I + 1) * PER <= NM * PER) __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+    sched_ld_mfma<I + 1, NM, PER, AHEAD>();
+  }
+}
+
 // Per-lane state of one wave: its 32 query rows (lane % 32) and the running
 // softmax of each.
 template <typename T, int D, int MODE>
@@ -208,13 +220,19 @@ struct RowState {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[bk][i] = 0.f;
     if constexpr (kBf) {
+      // The k-steps of a lane's K row differ only in XOR-swizzled chunk
+      // bits: koff[st] = koff[0] ^ 16 st.  The empty asm keeps the XORs here
+      // instead of eight registers hoisted out of the tile loop.
+      int kx = koff[0];
+      asm volatile("" : "+v"(kx));
 #pragma unroll
       for (int st = 0; st < kQSteps; ++st)
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + koff[st] + 32 * bk * G::kRowBytes);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + (kx ^ (16 * st)) + 32 * bk * G::kRowBytes);
           s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[bk], 0, 0, 0);
         }
+      sched_ld_mfma<0, 2 * kQSteps, 1, 4>();
     } else {
       const int krow0 = key_perm(n);
 #pragma unroll
@@ -282,6 +300,8 @@ struct RowState {
     l_run += ls;
 
     // ---- O^T += V^T P^T ----
+    int vx = voff[0];
+    if constexpr (D == 128) asm volatile("" : "+v"(vx));  // as for kx above
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk) {
       if constexpr (kBf) {
@@ -294,8 +314,8 @@ struct RowState {
           const unsigned char* vb = vl + (32 * bk + 16 * c2) * G::kRowBytes;
 #pragma unroll
           for (int md = 0; md < kDB; ++md) {
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + voff[md]));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + voff[kDB + md]));
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + vread_off(vx, 0, md)));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + vread_off(vx, 1, md)));
             const s16x4 both[2] = {lo, hi};
             const bf16x8 a = __builtin_bit_cast(bf16x8, both);
             acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[md], 0, 0, 0);
@@ -313,6 +333,15 @@ struct RowState {
         }
       }
     }
+    if constexpr (kBf) sched_ld_mfma<0, 4 * kDB, 2, 8>();
+  }
+
+  // Byte offset of the transposing V read (r, md) of this lane.  At
+  // head_dim 128 the reads differ only in swizzled chunk bits and a 4-row
+  // step: voff(r, md) = (voff(0, 0) ^ (64 md + 16 r)) + 4 r rows.
+  __device__ __forceinline__ int vread_off(int vx, int r, int md) const {
+    if constexpr (D == 128) return (vx ^ (64 * md + 16 * r)) + r * 4 * G::kRowBytes;
+    else return voff[r * kDB + md];
   }
 };
 
