@@ -8,7 +8,9 @@ with it.
 from .tree_attn_oracle import (  # noqa: F401
     ancestor_mask_page,
     masked_attention,
+    masked_attention_backward,
     prefill,
+    prefill_backward,
     decode,
     verify,
     plan_prefill,

@@ -145,6 +145,41 @@ def masked_attention(q, k, v, mask, scale: float):
     return o, lse
 
 
+def masked_attention_backward(q, k, v, do, mask, scale: float):
+    """Gradients of o = masked_attention(q, k, v, mask, scale) for the output
+    gradient do, written out from the definition in float64.
+
+    With S = scale q k^T (non-visible entries -inf), P = row softmax of S and
+    o = P v:
+      dv = P^T do,  dP = do v^T,  dS_ij = P_ij (dP_ij - sum_l P_il dP_il),
+      dq = scale dS k,  dk = scale dS^T q.
+    A KV head's gradients sum over the query heads that read it (GQA).
+    Returns dq [Tq, Hq, d], dk and dv [Tk, Hkv, d].
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    tq, hq, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(hq):
+        kh, vh = k[:, h // g, :], v[:, h // g, :]
+        for r0 in range(0, tq, _ROW_BLOCK):
+            r1 = min(tq, r0 + _ROW_BLOCK)
+            s = scale * (q[r0:r1, h, :] @ kh.T)
+            s = np.where(mask[r0:r1], s, -np.inf)
+            m = s.max(axis=1)
+            p = np.exp(s - m[:, None])
+            p /= p.sum(axis=1)[:, None]
+            dp = do[r0:r1, h, :] @ vh.T
+            ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+            dv[:, h // g, :] += p.T @ do[r0:r1, h, :]
+            dq[r0:r1, h, :] = scale * (ds @ kh)
+            dk[:, h // g, :] += scale * (ds.T @ q[r0:r1, h, :])
+    return dq, dk, dv
+
+
 def lse_merge(parts):
     """Combine attention results over disjoint key sets from (o, lse) pairs.
 
@@ -192,6 +227,26 @@ def prefill(desc, q, k, v, scale: float):
         mask = ancestor_mask_page(P, L, C)
         o[sl], lse[:, sl] = masked_attention(q[sl], k[sl], v[sl], mask, scale)
     return o, lse
+
+
+def prefill_backward(desc, q, k, v, do, scale: float):
+    """Gradients of the packed tree-varlen forward (``prefill``) with respect
+    to q, k and v for the output gradient do, page by page under the same
+    ancestor mask.  The training path the PaDoc summary describes
+    ("Training paradigm") differentiates exactly this forward.
+    Returns dq [T, Hq, d], dk and dv [T, Hkv, d] in float64."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for p, P, L, C, base in _page_offsets(desc.prefix_len, desc.n_regions, desc.layout_len, desc.content_len):
+        tp = P + sum(L) + sum(C)
+        if tp == 0:
+            continue
+        sl = slice(base, base + tp)
+        mask = ancestor_mask_page(P, L, C)
+        dq[sl], dk[sl], dv[sl] = masked_attention_backward(q[sl], k[sl], v[sl], do[sl], mask, scale)
+    return dq, dk, dv
 
 
 def decode(desc, q, k_main, v_main, k_suffix, v_suffix, scale: float, rows=None):

@@ -426,3 +426,84 @@ def test_verify_branches_are_isolated_and_match_sdpa():
             vv = np.concatenate([vc[ctx_off[p]:ctx_off[p + 1]], vt[path]])
             ref = sdpa64(q[node_off[b] + i:node_off[b] + i + 1], kk, vv, scale=0.5)
             assert np.max(np.abs(o[node_off[b] + i] - ref[0])) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# backward of the packed forward (the training path)
+# --------------------------------------------------------------------------
+
+def test_backward_matches_central_differences():
+    """Gradients of loss = sum(o * w) by central differences of the forward
+    (a property of the forward alone: no formula of the backward is used)."""
+    rng = np.random.default_rng(11)
+    desc = one_page(3, [2, 1], [3, 2])  # 11 tokens, two branches
+    T = desc.total_tokens()
+    q, k, v = rand(rng, T, 2, 4), rand(rng, T, 1, 4), rand(rng, T, 1, 4)
+    w = rand(rng, T, 2, 4)
+    scale = 0.7
+    dq, dk, dv = oracle.prefill_backward(desc, q, k, v, w, scale)
+
+    def loss(qq, kk, vv):
+        return float((oracle.prefill(desc, qq, kk, vv, scale)[0] * w).sum())
+
+    eps = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(**{"qq": args_p["q"], "kk": args_p["k"], "vv": args_p["v"]})
+                        - loss(**{"qq": args_m["q"], "kk": args_m["k"], "vv": args_m["v"]})) / (2 * eps)
+        assert np.max(np.abs(num - g)) < 1e-7, name
+
+
+def test_backward_matches_autograd_of_dense_masked_sdpa():
+    """torch autograd through the library SDPA routine (float64, mask built
+    by slicing, GQA by repeating KV heads) gives the same gradients."""
+    rng = np.random.default_rng(12)
+    pages = [(5, [2, 0, 3], [4, 0, 2]), (0, [1], [3]), (3, [], [])]
+    desc = synth.make_prefill_desc([p[0] for p in pages], [np.array(p[1]) for p in pages],
+                                   [np.array(p[2]) for p in pages])
+    T = desc.total_tokens()
+    q, k, v, do = rand(rng, T, 4, 8), rand(rng, T, 2, 8), rand(rng, T, 2, 8), rand(rng, T, 4, 8)
+    dq, dk, dv = oracle.prefill_backward(desc, q, k, v, do, 0.3)
+    base = 0
+    for P, L, C in pages:
+        t = P + sum(L) + sum(C)
+        sl = slice(base, base + t)
+        qt = torch.tensor(q[sl], requires_grad=True)
+        kt = torch.tensor(k[sl], requires_grad=True)
+        vt = torch.tensor(v[sl], requires_grad=True)
+        o = F.scaled_dot_product_attention(qt.transpose(0, 1), kt.repeat_interleave(2, dim=1).transpose(0, 1),
+                                           vt.repeat_interleave(2, dim=1).transpose(0, 1),
+                                           attn_mask=torch.as_tensor(mask_by_slicing(P, L, C)), scale=0.3)
+        o.transpose(0, 1).backward(torch.tensor(do[sl]))
+        assert np.max(np.abs(qt.grad.numpy() - dq[sl])) < 1e-11
+        assert np.max(np.abs(kt.grad.numpy() - dk[sl])) < 1e-11
+        assert np.max(np.abs(vt.grad.numpy() - dv[sl])) < 1e-11
+        base += t
+
+
+def test_backward_pages_and_unseen_keys_get_no_gradient():
+    """An output gradient on one page moves nothing on another page, and a
+    key no row with a non-zero output gradient can see gets exactly zero."""
+    rng = np.random.default_rng(13)
+    desc = synth.make_prefill_desc([4, 6], [np.array([2, 2]), np.array([1])], [np.array([3, 1]), np.array([5])])
+    T = desc.total_tokens()
+    t0 = 4 + 4 + 4  # tokens of page 0
+    q, k, v = rand(rng, T, 2, 8), rand(rng, T, 2, 8), rand(rng, T, 2, 8)
+    do = rand(rng, T, 2, 8)
+    do[t0:] = 0.0
+    # only the first branch's rows of page 0 carry a gradient: rows 8..10
+    # (branch 1 content); they see X (0..3), B_1 (4..5) and themselves
+    do[:8] = 0.0
+    do[11] = 0.0
+    dq, dk, dv = oracle.prefill_backward(desc, q, k, v, do, 0.5)
+    assert np.all(dq[t0:] == 0) and np.all(dk[t0:] == 0) and np.all(dv[t0:] == 0)
+    unseen = [6, 7, 11]  # B_2 and the second branch's content
+    assert np.all(dk[unseen] == 0) and np.all(dv[unseen] == 0)
+    assert np.all(np.abs(dv[[0, 1, 2, 3, 4, 5, 8, 9, 10]]).sum(axis=(1, 2)) > 0)
