@@ -68,6 +68,9 @@ extern "C" {
 #define TA_FIELD_DECODE_ROWS 6  /* decode:  [branches][5] main_start, main_len, suffix_start, suffix_len, position */
 #define TA_FIELD_VERIFY_MASK 7  /* verify:  [nodes] ancestor bitmask (bit j: node j of the same branch is an ancestor or itself) */
 #define TA_FIELD_VERIFY_ROWS 8  /* verify:  [nodes][4] ctx_start, ctx_len, tree_base (abs node 0 of the branch), position */
+#define TA_FIELD_BWD_WORK 10    /* prefill: [items][10] key-major backward items, same columns as TA_FIELD_WORK:
+                                   keys [row0, row0 + nrows), rows [a_lo, a_hi) and [b_lo, b_hi), flags in a_full's
+                                   place is not exported; tile_hi = row tiles walked */
 #define TA_FIELD_WORK 9         /* any:     [work][10] the launch work list: row0, nrows, a_lo, a_full, a_hi, b_lo, b_hi,
                                            partial slot (-1: direct), tile_lo, tile_hi (diagnostic; order is not contractual) */
 
@@ -187,6 +190,31 @@ int tree_attn_prefill(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hk
                       int32_t head_dim, float scale, const void* q, const void* k,
                       const void* v, void* o, float* lse, void* scratch,
                       size_t scratch_bytes, void* stream);
+
+/* Scratch bytes tree_attn_prefill_backward needs: two fp32 values per
+ * (query head, row) (the row sums Dd = sum_d dO * O and lse * log2 e). */
+int tree_attn_backward_scratch_bytes(const ta_plan* plan, int32_t hq, size_t* bytes);
+
+/* Backward of tree_attn_prefill: the gradients of o with respect to q, k and
+ * v for an output gradient d_o, under the same ancestor visibility (the
+ * training path of the PaDoc summary, "Training paradigm": the model trains
+ * through this masked forward).  With P the forward's softmax rows,
+ *   dv = P^T d_o,  dP = d_o v^T,  dS = P * (dP - rowsum(d_o * o)),
+ *   dq = scale dS k,  dk = scale dS^T q   (KV-head gradients summed over the
+ *   query heads of the group).
+ * Inputs: q, o, d_o [rows, Hq, d]; k, v [rows, Hkv, d]; lse [Hq, rows] fp32
+ * as tree_attn_prefill wrote it (natural log), all from the same call.
+ * Outputs (caller-owned, overwritten): dq [rows, Hq, d], dk and dv
+ * [rows, Hkv, d], in the input dtype.  bf16 only (TA_DTYPE_F32 returns
+ * UNSUPPORTED).  The plan must be uploaded and not balanced (STATE
+ * otherwise).  scratch: >= tree_attn_backward_scratch_bytes, 256-byte
+ * aligned.  Three kernels on `stream` (row sums, dq query-major, dk/dv
+ * key-major); deterministic, no atomics. */
+int tree_attn_prefill_backward(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
+                               int32_t head_dim, float scale, const void* q, const void* k,
+                               const void* v, const void* o, const float* lse, const void* d_o,
+                               void* dq, void* dk, void* dv, void* scratch,
+                               size_t scratch_bytes, void* stream);
 
 /* Cascade branch decode over a decode plan: pass 1 streams each page's main
  * KV once for all of its branches and query heads and each branch's suffix,

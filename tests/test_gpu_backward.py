@@ -1,0 +1,106 @@
+"""GPU parity of the prefill backward (dq, dk, dv) against the fp64 oracle.
+
+The oracle differentiates its own fp64 forward, so the comparison covers the
+whole bf16 training path: forward (o, lse) and backward on the GPU.
+Tolerance: bf16 operands of the backward products (P and dS are rounded to
+bf16 before their MFMAs, the gradients are written in bf16) give errors
+proportional to each gradient tensor's size, so every element must satisfy
+|gpu - ref| <= 2e-2 * max|ref| + 1e-2 * |ref| (the forward's bf16 tolerance
+with the absolute term taken relative to the tensor's scale).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tree_structured_attention_amd import binding as ta
+from tree_structured_attention_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def close_scaled(got, ref, what, atol_frac=2e-2, rtol=1e-2):
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    err = np.abs(got - ref)
+    bad = err > atol_frac * scale + rtol * np.abs(ref)
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - (atol_frac * scale + rtol * np.abs(ref))), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst at {i}: "
+                             f"gpu={got[i]!r} ref={ref[i]!r} max_abs={err.max():.3g} scale={scale:.3g}")
+    return float(err.max() / max(scale, 1e-30))
+
+
+def make(pages, hq, hkv, d, seed):
+    rng = np.random.default_rng(seed)
+    desc = synth.make_prefill_desc([p[0] for p in pages], [np.array(p[1]) for p in pages],
+                                   [np.array(p[2]) for p in pages])
+    t = synth.prefill_tensors(rng, desc, hq, hkv, d, torch.bfloat16)
+    g = torch.from_numpy(rng.standard_normal((desc.total_tokens(), hq, d), dtype=np.float32)).to(torch.bfloat16)
+    return desc, t, g
+
+
+def gpu_backward(desc, t, g, scale, plan=None):
+    plan = plan or ta.plan_for(desc).upload()
+    q, k, v, do = (x.cuda().contiguous() for x in (t["q"], t["k"], t["v"], g))
+    o, lse = ta.prefill(plan, q, k, v, scale=scale)
+    dq, dk, dv = ta.prefill_backward(plan, q, k, v, o, lse, do, scale=scale)
+    torch.cuda.synchronize()
+    return dq.float().cpu().numpy(), dk.float().cpu().numpy(), dv.float().cpu().numpy()
+
+
+CASES = [
+    # ragged: several row and key tiles, empty layout units and branches,
+    # branches shorter and longer than a 64-token tile, many short branches
+    [(200, [3, 0, 5, 2, 1], [70, 0, 9, 130, 1]), (0, [4], [3]), (65, [], [])],
+    [(37, [1] * 12, [5, 6, 7, 1, 2, 3, 4, 5, 6, 7, 8, 9])],
+    [(1, [0], [200])],
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("heads", [(16, 8, 128), (8, 8, 64), (8, 2, 32), (4, 1, 128)])
+def test_backward_small(case, heads):
+    hq, hkv, d = heads
+    desc, t, g = make(CASES[case], hq, hkv, d, seed=31 * case + d)
+    scale = 1.0 / np.sqrt(d)
+    say(f"[backward] case {case} rows={desc.total_tokens()} heads={heads}")
+    dq, dk, dv = gpu_backward(desc, t, g, scale)
+    rq, rk, rv = oracle.prefill_backward(desc, t["q"], t["k"], t["v"], g, scale)
+    eq = close_scaled(dq, rq, "dq")
+    ek = close_scaled(dk, rk, "dk")
+    ev = close_scaled(dv, rv, "dv")
+    say(f"    max_abs/scale dq={eq:.3g} dk={ek:.3g} dv={ev:.3g}")
+
+
+def test_backward_deterministic_and_page_isolated():
+    """Two runs are bit-identical, and an output gradient confined to one page
+    leaves every gradient of the other pages exactly zero."""
+    desc, t, g = make(CASES[0], 16, 8, 128, seed=5)
+    n0 = 200 + 11 + 210  # tokens of page 0
+    g[n0:] = 0
+    a = gpu_backward(desc, t, g, 0.088)
+    b = gpu_backward(desc, t, g, 0.088)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    for x in a:
+        assert np.all(x[n0:] == 0)
+
+
+def test_backward_rejects_balanced_plan_and_fp32():
+    desc, t, g = make(CASES[2], 16, 8, 128, seed=6)
+    q, k, v, do = (x.cuda().contiguous() for x in (t["q"], t["k"], t["v"], g))
+    plan = ta.plan_for(desc).upload()
+    o, lse = ta.prefill(plan, q, k, v)
+    with pytest.raises(ta.TreeAttnError) as e:
+        ta.prefill_backward(plan, q.float(), k.float(), v.float(), o.float(), lse, do.float())
+    assert e.value.code == ta.TA_ERR_UNSUPPORTED
+    bal = ta.plan_for(desc).balance(8, 4096)
+    if bal.info["n_partials"] > 0:
+        bal.upload()
+        with pytest.raises(ta.TreeAttnError) as e:
+            ta.prefill_backward(bal, q, k, v, o, lse, do)
+        assert e.value.code == ta.TA_ERR_STATE

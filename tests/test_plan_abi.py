@@ -15,7 +15,7 @@ from tree_structured_attention_amd import synth
 def test_library_exports_every_declared_symbol():
     L = ta.lib()
     declared = ta.header_symbols()
-    assert len(declared) == 14
+    assert len(declared) == 16
     for name in declared:
         assert hasattr(L, name), name
     assert L.tree_attn_version().decode().startswith("tree_attn")
@@ -41,7 +41,40 @@ def check_prefill_plan(desc):
     for w in work:
         cover[w[0]:w[0] + w[1]] += 1
     assert (cover == 1).all()
+    check_backward_items(desc, plan)
     return plan
+
+
+def check_backward_items(desc, plan):
+    """Key-major items of the backward: every key lies in exactly one item,
+    inside one page region (main stream or branch area), and every row that
+    can see a key lies in one of its item's row segments."""
+    items = plan.export("bwd_work")
+    T = desc.total_tokens()
+    owner = np.full(T, -1, np.int64)
+    for n, w in enumerate(items):
+        k0, nk = int(w[0]), int(w[1])
+        assert 0 < nk <= 64
+        assert (owner[k0:k0 + nk] == -1).all()
+        owner[k0:k0 + nk] = n
+    assert (owner >= 0).all()
+    base = 0
+    for p, sl in desc.page_slices():
+        P = int(desc.prefix_len[p])
+        L, C = desc.layout_len[sl], desc.content_len[sl]
+        M, t = P + int(L.sum()), P + int(L.sum()) + int(C.sum())
+        mask = oracle.ancestor_mask_page(P, L, C)
+        keys = range(t) if t <= 2048 else range(0, t, 37)  # every key of small pages, a sample of large ones
+        for j in keys:
+            w = items[owner[base + j]]
+            k0, nk, flags = int(w[0]), int(w[1]), int(w[3])
+            in_branch = base + j >= base + M
+            assert bool(flags & 2) == in_branch
+            assert (k0 >= base + M) == in_branch and (k0 + nk <= base + M or in_branch)
+            rows = base + np.nonzero(mask[:, j])[0]
+            seg = ((rows >= w[2]) & (rows < w[4])) | ((rows >= w[5]) & (rows < w[6]))
+            assert seg.all(), (p, j)
+        base += t
 
 
 def test_prefill_plan_configs_exact():

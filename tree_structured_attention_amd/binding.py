@@ -49,8 +49,9 @@ FIELD = {
     "verify_mask": 7,
     "verify_rows": 8,
     "work": 9,
+    "bwd_work": 10,
 }
-FIELD_WIDTH = {"pages": 5, "branches": 3, "decode_rows": 5, "verify_rows": 4, "work": 10}
+FIELD_WIDTH = {"pages": 5, "branches": 3, "decode_rows": 5, "verify_rows": 4, "work": 10, "bwd_work": 10}
 
 
 class TreeAttnError(RuntimeError):
@@ -109,6 +110,9 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_int),
             "tree_attn_verify": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
                                  ctypes.c_int),
+            "tree_attn_backward_scratch_bytes": ([_P, i32, ctypes.POINTER(sz)], ctypes.c_int),
+            "tree_attn_prefill_backward": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz,
+                                            _P], ctypes.c_int),
             "tree_attn_last_error": ([], ctypes.c_char_p),
             "tree_attn_version": ([], ctypes.c_char_p),
         }
@@ -364,3 +368,32 @@ def verify(plan: Plan, q, k_ctx, v_ctx, k_tree, v_tree, scale=None, want_lse=Tru
                                   _dev_ptr(k_ctx), _dev_ptr(v_ctx), _dev_ptr(k_tree), _dev_ptr(v_tree),
                                   _dev_ptr(o), _dev_ptr(l), sp, sn, _stream_handle(stream)))
     return o, l
+
+
+def backward_scratch_bytes(plan: Plan, hq: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().tree_attn_backward_scratch_bytes(plan.handle, hq, ctypes.byref(n)))
+    return int(n.value)
+
+
+def prefill_backward(plan: Plan, q, k, v, o, lse, d_o, scale=None, dq=None, dk=None, dv=None,
+                     scratch: Optional[torch.Tensor] = None, stream=None):
+    """Gradients (dq, dk, dv) of the packed forward for output gradient d_o;
+    o and lse are the forward's outputs for the same q, k, v."""
+    hq, hkv, d = _heads(q, k)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = backward_scratch_bytes(plan, hq)
+    if scratch is None and need:
+        scratch = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    sp, sn = None, 0
+    if need:
+        off = (-scratch.data_ptr()) % 256
+        view = scratch[off:]
+        sp, sn = ctypes.c_void_p(view.data_ptr()), view.numel()
+    _check(lib().tree_attn_prefill_backward(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
+                                            _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(lse), _dev_ptr(d_o),
+                                            _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv), sp, sn,
+                                            _stream_handle(stream)))
+    return dq, dk, dv

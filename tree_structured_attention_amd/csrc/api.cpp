@@ -150,6 +150,13 @@ extern "C" int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t
     case TA_FIELD_DECODE_ROWS: if (k == TA_PLAN_DECODE) src = &plan->decode_rows5; break;
     case TA_FIELD_VERIFY_MASK: if (k == TA_PLAN_VERIFY) src = &plan->verify_mask; break;
     case TA_FIELD_VERIFY_ROWS: if (k == TA_PLAN_VERIFY) src = &plan->verify_rows4; break;
+    case TA_FIELD_BWD_WORK:
+      if (k != TA_PLAN_PREFILL) break;
+      for (const WorkItem& w : plan->kwork)
+        work_tmp.insert(work_tmp.end(), {w.row0, w.nrows, w.a_lo, w.flags, w.a_hi, w.b_lo, w.b_hi, w.out,
+                                         w.tile_lo, w.tile_hi});
+      src = &work_tmp;
+      break;
     case TA_FIELD_WORK:
       for (const WorkItem& w : plan->work)
         work_tmp.insert(work_tmp.end(), {w.row0, w.nrows, w.a_lo, w.a_full, w.a_hi, w.b_lo, w.b_hi, w.out,
@@ -289,4 +296,64 @@ extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, 
   rc = hip_status(launch_attention(kDecode, dtype, p, int(plan->work.size()), head_dim, st), "decode launch");
   if (rc) return rc;
   return hip_status(launch_merge_for(plan, dtype, p, head_dim, st), "decode merge launch");
+}
+
+extern "C" int tree_attn_backward_scratch_bytes(const ta_plan* plan, int32_t hq, size_t* bytes) {
+  if (!plan || !bytes) return fail(TA_ERR_INVALID_ARG, "backward_scratch_bytes: NULL argument");
+  if (hq <= 0) return fail(TA_ERR_INVALID_ARG, "backward_scratch_bytes: hq must be positive");
+  *bytes = size_t(2 * align256(plan->n_rows * hq * 4));
+  return TA_OK;
+}
+
+extern "C" int tree_attn_prefill_backward(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
+                                          int32_t head_dim, float scale, const void* q, const void* k, const void* v,
+                                          const void* o, const float* lse, const void* d_o, void* dq, void* dk,
+                                          void* dv, void* scratch, size_t scratch_bytes, void* stream) {
+  int rc = check_plan(plan, TA_PLAN_PREFILL, "prefill_backward");
+  if (rc) return rc;
+  if ((rc = check_heads(dtype, hq, hkv, head_dim, scale))) return rc;
+  if (dtype != TA_DTYPE_BF16) return fail(TA_ERR_UNSUPPORTED, "prefill_backward: only TA_DTYPE_BF16 is built");
+  if (plan->n_partials > 0) return fail(TA_ERR_STATE, "prefill_backward: the plan is balanced; build an unbalanced one");
+  const int64_t rows = plan->n_rows;
+  if ((rc = check_tensor(q, rows, "q")) || (rc = check_tensor(k, rows, "k")) || (rc = check_tensor(v, rows, "v")) ||
+      (rc = check_tensor(o, rows, "o")) || (rc = check_tensor(d_o, rows, "d_o")) || (rc = check_tensor(dq, rows, "dq")) ||
+      (rc = check_tensor(dk, rows, "dk")) || (rc = check_tensor(dv, rows, "dv")))
+    return rc;
+  if (rows > 0 && !lse) return fail(TA_ERR_INVALID_ARG, "prefill_backward: lse is NULL");
+  if (lse && !aligned(lse, 4)) return fail(TA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const int64_t half = align256(rows * hq * 4);
+  if (rows > 0) {
+    if (!scratch) return fail(TA_ERR_WORKSPACE, "prefill_backward: scratch is NULL");
+    if (!aligned(scratch, 256)) return fail(TA_ERR_INVALID_ARG, "prefill_backward: scratch must be 256-byte aligned");
+    if (int64_t(scratch_bytes) < 2 * half)
+      return fail(TA_ERR_WORKSPACE, "prefill_backward: scratch smaller than tree_attn_backward_scratch_bytes");
+  }
+  if ((rc = check_uploaded(plan, "prefill_backward"))) return rc;
+  if (rows == 0) return TA_OK;
+  const unsigned char* dev = static_cast<const unsigned char*>(plan->dev);
+  BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dO = d_o;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.lse = lse;
+  p.l2 = static_cast<float*>(scratch);
+  p.dd = reinterpret_cast<float*>(static_cast<unsigned char*>(scratch) + half);
+  p.work = reinterpret_cast<const WorkItem*>(dev + plan->layout.work);
+  p.kwork = reinterpret_cast<const WorkItem*>(dev + plan->layout.kwork);
+  p.row_a = reinterpret_cast<const int32_t*>(dev + plan->layout.row_a);
+  p.row_b = reinterpret_cast<const int32_t*>(dev + plan->layout.row_b);
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  p.c = scale * 1.4426950408889634f;
+  p.scale = scale;
+  p.n_rows = rows;
+  return hip_status(launch_backward(p, int(plan->work.size()), int(plan->kwork.size()), head_dim,
+                                    static_cast<hipStream_t>(stream)),
+                    "prefill_backward launch");
 }

@@ -32,143 +32,9 @@
 // unless it is a non-finite V of a key another row of the same tile needs.
 // fp32 inputs use v_mfma_f32_32x32x2f32 with the same tiling (no
 // down-conversion).
-#include <hip/hip_runtime.h>
-
-#include <cmath>
-#include <cstdint>
-#include <type_traits>
-
-#include "ta_kernels.h"
+#include "ta_device.h"
 
 namespace ta {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
-
-// ---------------------------------------------------------------------------
-// small device helpers
-// ---------------------------------------------------------------------------
-
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Row maximum / sum across the two lanes (l, l + 32) that share a query row.
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// MFMA row m of a 32-key block holds physical key pi(m): bits 2 and 3 swapped.
-__device__ __forceinline__ int key_perm(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-// Accumulator register i of a lane in half h holds (within the 32-key block)
-// physical key 16 * (i / 8) + 8 * h + (i % 8).
-__device__ __forceinline__ int reg_key(int i, int h) { return 16 * (i >> 3) + 8 * h + (i & 7); }
-
-typedef __attribute__((ext_vector_type(2))) float f32x2v;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
-
-// Two fp32 -> bf16 (round to nearest even) in one packed convert.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const f32x2v f = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
-}
-
-template <typename T>
-struct Elt;
-template <>
-struct Elt<__bf16> {
-  static constexpr int kBytes = 2;
-};
-template <>
-struct Elt<float> {
-  static constexpr int kBytes = 4;
-};
-
-// LDS geometry of one 64-key tile: K and V row-major, one row per key, no
-// padding.  The 16-byte chunks of a row are XOR-swizzled,
-//   position = chunk ^ swz(row),
-// with swz a bijection of the low row bits (for 16 chunks per row: the
-// 4-bit row index rotated by 2).  Then the 16 K rows of an MFMA operand read
-// land in 16 different chunk positions, and in a transposing V read the two
-// 16-lane groups that share 4 rows touch 16 distinct positions (no bank
-// conflicts).  swz depends only on row % 16, so whole 16-row steps are plain
-// immediate offsets.
-template <typename T, int D>
-struct TileGeom {
-  static constexpr int kRowBytes = D * Elt<T>::kBytes;
-  static constexpr int kChunks = kRowBytes / 16;
-  static constexpr int kTileBytes = kKeyTile * kRowBytes;
-  static constexpr int kStageBytes = 2 * kTileBytes;  // K then V
-  __device__ static __forceinline__ int swz(int row) {
-    if constexpr (kChunks == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else if constexpr (kChunks == 8) return ((row & 1) << 2) | ((row >> 1) & 3);
-    else return ((row & 1) << 1) | ((row >> 1) & 1);
-  }
-  // byte offset of (row, byte-in-row) inside a K or V tile
-  __device__ static __forceinline__ int at(int row, int byte) {
-    return row * kRowBytes + ((((byte >> 4) ^ swz(row)) << 4) | (byte & 15));
-  }
-};
-
-// Global -> LDS copy of one 64-key K/V tile with buffer loads that write LDS
-// directly.  The buffer resource covers only the keys of the segment still
-// to be read, so rows past its end load as zeros (no branches).
-template <typename T, int D, int NW>
-struct TileLoader {
-  using G = TileGeom<T, D>;
-  static constexpr int kRowsPerInst = 64 / G::kChunks;
-  static constexpr int kInsts = kKeyTile / (kRowsPerInst * NW);
-  static_assert(kInsts * kRowsPerInst * NW == kKeyTile, "tile split");
-  int voff[kInsts];  // per-lane byte offset into the tile's key rows
-
-  __device__ __forceinline__ void init(int lane, int wave, int64_t row_stride) {
-#pragma unroll
-    for (int j = 0; j < kInsts; ++j) {
-      const int row = (j * NW + wave) * kRowsPerInst + lane / G::kChunks;
-      const int chunk = (lane % G::kChunks) ^ G::swz(row);
-      voff[j] = int(row * row_stride) + chunk * 16;
-    }
-  }
-
-  __device__ __forceinline__ void issue(unsigned char* stage, const unsigned char* kbase, const unsigned char* vbase,
-                                        int t0, int t1, int64_t row_stride, int wave) const {
-    const int rows = min(t1 - t0, kKeyTile);
-    const int nbytes = rows > 0 ? int(rows * row_stride) : 0;
-    __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase) + int64_t(t0) * row_stride, (short)0, nbytes, 0x00020000);
-    __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase) + int64_t(t0) * row_stride, (short)0, nbytes, 0x00020000);
-#pragma unroll
-    for (int j = 0; j < kInsts; ++j) {
-      const int row0 = (j * NW + wave) * kRowsPerInst;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + row0 * G::kRowBytes), 16, voff[j], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + G::kTileBytes + row0 * G::kRowBytes), 16,
-                                               voff[j], 0, 0, 0);
-    }
-  }
-};
-
-// Scheduling groups: AHEAD LDS reads up front, then per matrix instruction
-// one MFMA and the PER reads of a later one.
-template <int I, int NM, int PER, int AHEAD>
-__device__ __forceinline__ void sched_ld_mfma() {
-  if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
-  if constexpr (I < NM) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (AHEAD + (I + 1) * PER <= NM * PER) __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
-    sched_ld_mfma<I + 1, NM, PER, AHEAD>();
-  }
-}
 
 // Per-lane state of one wave: its 32 query rows (lane % 32) and the running
 // softmax of each.

@@ -1,0 +1,458 @@
+// HIP kernels for the backward of packed tree-varlen attention (gfx950).
+//
+// The gradients of o = softmax(scale q k^T, masked) v for an output
+// gradient dO follow from the definition (PaDoc summary, "Training
+// paradigm": the model trains through exactly this masked forward):
+//   P = exp(scale q k^T - lse)   (lse saved by the forward)
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Dd),  Dd = rowsum(dO * O)
+//   dQ = scale dS K,  dK = scale dS^T Q
+// Three launches:
+//   bwd_prep_kernel   Dd and lse * log2(e) per (query head, row), fp32
+//   bwd_dq_kernel     query-major, over the forward's row tiles: recomputes
+//                     S^T = K Q^T and dP^T = V dO^T per 64-key tile and adds
+//                     K^T dS^T into dQ^T held in registers
+//   bwd_dkdv_kernel   key-major, over the plan's key tiles: each wave holds
+//                     32 keys of one KV head and walks the 64-row tiles (and
+//                     every query head of the group) that can see them,
+//                     adding dO^T P into dV^T and Q^T dS into dK^T
+// Both main kernels use the forward's MFMA formulations: an operand read
+// from an LDS tile in permuted row order against one held in registers
+// (v_mfma_f32_32x32x16_bf16), and a transposing LDS read (ds_read_b64_tr_b16)
+// against a product taken straight from accumulators.  No atomics: each
+// output element is written by exactly one wave, so results are
+// deterministic.
+#include "ta_device.h"
+
+namespace ta {
+
+// One (row, query head) per 64-lane group: Dd = sum_d dO * O and the
+// forward's lse converted to log2 units.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  constexpr int kPer = D / 64 > 0 ? D / 64 : 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (pair >= p.n_rows * p.hq) return;
+  const int64_t row = pair / p.hq;
+  const int head = int(pair % p.hq);
+  const __bf16* o = reinterpret_cast<const __bf16*>(p.o) + (row * p.hq + head) * D;
+  const __bf16* g = reinterpret_cast<const __bf16*>(p.dO) + (row * p.hq + head) * D;
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int d = lane + 64 * j;
+    if (d < D) s += float(o[d]) * float(g[d]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) {
+    const int64_t idx = int64_t(head) * p.n_rows + row;
+    p.dd[idx] = s;
+    p.l2[idx] = p.lse[idx] * 1.4426950408889634f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: query-major
+// ---------------------------------------------------------------------------
+
+// GH query heads of one KV head per workgroup, 32 / GH tokens per wave, a
+// 64-token row tile per work item (the forward's tiling and segments).
+template <int D, int GH>
+__global__ __launch_bounds__(128 * GH, 2) void bwd_dq_kernel(BwdParams p) {
+  using T = __bf16;
+  using G = TileGeom<T, D>;
+  constexpr int NW = 2 * GH;
+  constexpr int TPW = 32 / GH;
+  constexpr int kQSteps = D / 16;
+  constexpr int kDB = D / 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[G::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[G::kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int kvh = int(blockIdx.x % unsigned(p.hkv));
+  const WorkItem wi = p.work[blockIdx.x / unsigned(p.hkv)];
+  const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
+  const int n_tiles = n_a + (wi.b_hi - wi.b_lo + kKeyTile - 1) / kKeyTile;
+  const int fa = min(n_a, max(0, wi.a_full - wi.a_lo) / kKeyTile);
+  const int64_t kv_stride = int64_t(p.hkv) * D * 2;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + int64_t(kvh) * D * 2;
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + int64_t(kvh) * D * 2;
+
+  TileLoader<T, D, NW> loader;
+  loader.init(lane, wave, kv_stride);
+  auto tile0 = [&](int it) { return it < n_a ? wi.a_lo + it * kKeyTile : wi.b_lo + (it - n_a) * kKeyTile; };
+  auto tile_hi = [&](int it) { return it < n_a ? wi.a_hi : wi.b_hi; };
+  if (n_tiles > 0) loader.issue(lds0, kbase, vbase, tile0(0), tile_hi(0), kv_stride, wave);
+
+  const int h = lane >> 5, n = lane & 31;
+  const int tok = wave * TPW + n / GH;
+  const int head = kvh * p.group + int(blockIdx.y) * GH + (n % GH);
+  const bool row_ok = tok < wi.nrows;
+  const int row = wi.row0 + tok;
+  int ra = 0, rb = 0;
+  float l2 = 0.f, dd = 0.f;
+  bf16x8 qf[kQSteps], df[kQSteps];
+  {
+    const T* qrow = reinterpret_cast<const T*>(p.q) + (int64_t(row) * p.hq + head) * D + (D / 2) * h;
+    const T* grow = reinterpret_cast<const T*>(p.dO) + (int64_t(row) * p.hq + head) * D + (D / 2) * h;
+#pragma unroll
+    for (int s = 0; s < kQSteps; ++s) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (row_ok) {
+        a = *reinterpret_cast<const u32x4*>(qrow + 8 * s);
+        b = *reinterpret_cast<const u32x4*>(grow + 8 * s);
+      }
+      qf[s] = __builtin_bit_cast(bf16x8, a);
+      df[s] = __builtin_bit_cast(bf16x8, b);
+    }
+    if (row_ok) {
+      ra = p.row_a[row];
+      rb = p.row_b[row];
+      l2 = p.l2[int64_t(head) * p.n_rows + row];
+      dd = p.dd[int64_t(head) * p.n_rows + row];
+    }
+  }
+  // LDS operand offsets (as in the forward): K / V rows in permuted MFMA
+  // row order for S^T and dP^T; transposing reads of K for dQ^T
+  const int krow0 = key_perm(n);
+  const int kx = G::at(krow0, D * h);
+  int voff[2 * kDB];
+  {
+    const int m16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int md = 0; md < kDB; ++md)
+        voff[r * kDB + md] = G::at(8 * (grp >> 1) + 4 * r + (m16 >> 2), 2 * (32 * md + 16 * (grp & 1) + 4 * (m16 & 3)));
+  }
+  f32x16 acc[kDB];
+#pragma unroll
+  for (int md = 0; md < kDB; ++md)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[md][i] = 0.f;
+  const bool wave_active = wave * TPW < wi.nrows;
+
+  auto consume = [&](const unsigned char* kl, const unsigned char* vl, int it) {
+    const bool seg_a = it < n_a;
+    const int t0 = tile0(it), t_hi = tile_hi(it);
+    const bool masked = seg_a ? it >= fa : true;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int st = 0; st < kQSteps; ++st) {
+        const int off = (kx ^ (16 * st)) + 32 * bk * G::kRowBytes;
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kl + off), qf[st], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vl + off), df[st], dp, 0, 0, 0);
+      }
+      // dS^T = P^T (dP^T - Dd), P^T = 2^(s c - lse2); invisible pairs get 0
+      u32x4 pk[2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float ds[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = 2 * j + e;
+          const int key = t0 + 32 * bk + reg_key(i, h);
+          bool vis = true;
+          if (masked) {
+            vis = key < t_hi;
+            if (seg_a) vis = vis & (key < ra);
+            else vis = vis & (key >= rb) & (key <= row);
+          }
+          const float pr = vis ? fast_exp2(fmaf(s[i], p.c, -l2)) : 0.f;
+          ds[e] = pr * (dp[i] - dd);
+        }
+        pk[j >> 2][j & 3] = pack_bf16x2(ds[0], ds[1]);
+      }
+      // dQ^T += K^T dS^T over the 32 keys of this block
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[c2]);
+        const unsigned char* kb = kl + (32 * bk + 16 * c2) * G::kRowBytes;
+#pragma unroll
+        for (int md = 0; md < kDB; ++md) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(kb + voff[md]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(kb + voff[kDB + md]));
+          const s16x4 both[2] = {lo, hi};
+          acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb, acc[md], 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto step = [&](int it, const unsigned char* cur, unsigned char* nxt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies into cur are done
+    __syncthreads();                     // ... and every wave's; reads of nxt are retired
+    if (it + 1 < n_tiles) loader.issue(nxt, kbase, vbase, tile0(it + 1), tile_hi(it + 1), kv_stride, wave);
+    if (wave_active) consume(cur, cur + G::kTileBytes, it);
+  };
+#pragma unroll 1
+  for (int it = 0; it < n_tiles; it += 2) {
+    step(it, lds0, lds1);
+    if (it + 1 < n_tiles) step(it + 1, lds1, lds0);
+  }
+
+  if (!row_ok) return;
+  T* dst = reinterpret_cast<T*>(p.dq) + (int64_t(row) * p.hq + head) * D;
+#pragma unroll
+  for (int md = 0; md < kDB; ++md)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * md + 8 * g + 4 * h;
+      u32x2 w = {pack_bf16x2(acc[md][4 * g] * p.scale, acc[md][4 * g + 1] * p.scale),
+                 pack_bf16x2(acc[md][4 * g + 2] * p.scale, acc[md][4 * g + 3] * p.scale)};
+      *reinterpret_cast<u32x2*>(dst + d0) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: key-major
+// ---------------------------------------------------------------------------
+
+// Per-row values of a 64-row tile staged beside its Q and dO tiles.
+struct RowMeta {
+  float l2[64], dd[64];
+  int32_t ra[64], rb[64];
+};
+
+// Two waves of 32 keys (one 64-key tile of one KV head) per workgroup; one
+// wave per SIMD, so the two accumulators dK^T, dV^T and the key's K and V
+// operands stay in registers.
+template <int D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BwdParams p) {
+  using T = __bf16;
+  using G = TileGeom<T, D>;
+  constexpr int NW = 2;
+  constexpr int kQSteps = D / 16;
+  constexpr int kDB = D / 32;
+  constexpr int kStage = G::kStageBytes + int(sizeof(RowMeta));
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int kvh = int(blockIdx.x % unsigned(p.hkv));
+  const WorkItem wi = p.kwork[blockIdx.x / unsigned(p.hkv)];
+  const bool branch_keys = (wi.flags & kKeyBranch) != 0;
+  const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
+  const int n_rt = n_a + (wi.b_hi - wi.b_lo + kKeyTile - 1) / kKeyTile;  // row tiles per query head
+  const int n_steps = n_rt * p.group;                                      // (head, row tile) pairs
+  const int64_t q_stride = int64_t(p.hq) * D * 2;
+  auto rt0 = [&](int r) { return r < n_a ? wi.a_lo + r * kKeyTile : wi.b_lo + (r - n_a) * kKeyTile; };
+  auto rt_hi = [&](int r) { return r < n_a ? wi.a_hi : wi.b_hi; };
+
+  TileLoader<T, D, NW> loader;
+  loader.init(lane, wave, q_stride);
+  // step s = (query head j of the group, row tile r): Q and dO tiles go to
+  // the stage by DMA; the row values by wave 0, through registers
+  auto issue = [&](int s, unsigned char* stage) {
+    const int j = s / n_rt, r = s % n_rt;
+    const int head = kvh * p.group + j;
+    const unsigned char* qb = reinterpret_cast<const unsigned char*>(p.q) + int64_t(head) * D * 2;
+    const unsigned char* gb = reinterpret_cast<const unsigned char*>(p.dO) + int64_t(head) * D * 2;
+    loader.issue(stage, qb, gb, rt0(r), rt_hi(r), q_stride, wave);
+  };
+  auto load_meta = [&](int s, float4& a, float4& b, int4& c, int4& d) {
+    const int j = s / n_rt, r = s % n_rt;
+    const int head = kvh * p.group + j;
+    const int r0 = rt0(r), rhi = min(rt_hi(r), r0 + kKeyTile);
+    const int x = r0 + 4 * (lane & 15);
+    const int64_t hb = int64_t(head) * p.n_rows;
+    float l[4], e[4];
+    int u[4], w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bool ok = x + t < rhi;
+      l[t] = ok ? p.l2[hb + x + t] : 0.f;
+      e[t] = ok ? p.dd[hb + x + t] : 0.f;
+      u[t] = ok ? p.row_a[x + t] : 0;
+      w[t] = ok ? p.row_b[x + t] : 0;
+    }
+    a = make_float4(l[0], l[1], l[2], l[3]);
+    b = make_float4(e[0], e[1], e[2], e[3]);
+    c = make_int4(u[0], u[1], u[2], u[3]);
+    d = make_int4(w[0], w[1], w[2], w[3]);
+  };
+  auto store_meta = [&](unsigned char* stage, const float4& a, const float4& b, const int4& c, const int4& d) {
+    RowMeta* m = reinterpret_cast<RowMeta*>(stage + G::kStageBytes);
+    const int x = 4 * (lane & 15);
+    *reinterpret_cast<float4*>(&m->l2[x]) = a;
+    *reinterpret_cast<float4*>(&m->dd[x]) = b;
+    *reinterpret_cast<int4*>(&m->ra[x]) = c;
+    *reinterpret_cast<int4*>(&m->rb[x]) = d;
+  };
+
+  // this wave's 32 keys as B operands (lane: key n, dims (D/2) h + 8 st ..)
+  const int h = lane >> 5, n = lane & 31;
+  const int key = wi.row0 + 32 * wave + n;
+  const bool key_ok = 32 * wave + n < wi.nrows;
+  bf16x8 kf[kQSteps], vf[kQSteps];
+  {
+    const T* krow = reinterpret_cast<const T*>(p.k) + (int64_t(key) * p.hkv + kvh) * D + (D / 2) * h;
+    const T* vrow = reinterpret_cast<const T*>(p.v) + (int64_t(key) * p.hkv + kvh) * D + (D / 2) * h;
+#pragma unroll
+    for (int s = 0; s < kQSteps; ++s) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (key_ok) {
+        a = *reinterpret_cast<const u32x4*>(krow + 8 * s);
+        b = *reinterpret_cast<const u32x4*>(vrow + 8 * s);
+      }
+      kf[s] = __builtin_bit_cast(bf16x8, a);
+      vf[s] = __builtin_bit_cast(bf16x8, b);
+    }
+  }
+  const int qx = G::at(key_perm(n), D * h);  // permuted-row operand reads of Q and dO
+  int toff[2 * kDB];                          // transposing reads of dO and Q
+  {
+    const int m16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int md = 0; md < kDB; ++md)
+        toff[r * kDB + md] = G::at(8 * (grp >> 1) + 4 * r + (m16 >> 2), 2 * (32 * md + 16 * (grp & 1) + 4 * (m16 & 3)));
+  }
+  f32x16 dk[kDB], dv[kDB];
+#pragma unroll
+  for (int md = 0; md < kDB; ++md)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk[md][i] = 0.f;
+      dv[md][i] = 0.f;
+    }
+
+  auto consume = [&](const unsigned char* stage, int s) {
+    const unsigned char* qt = stage;
+    const unsigned char* gt = stage + G::kTileBytes;
+    const RowMeta* m = reinterpret_cast<const RowMeta*>(stage + G::kStageBytes);
+    const int r = s % n_rt;
+    const int r0 = rt0(r), rhi = rt_hi(r);
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      // S = Q K^T and dP = dO V^T for rows [32 b2, 32 b2 + 32) of the tile:
+      // lane (key n, h) holds rows 32 b2 + reg_key(i, h)
+      f32x16 sc = {}, dp = {};
+#pragma unroll
+      for (int st = 0; st < kQSteps; ++st) {
+        const int off = (qx ^ (16 * st)) + 32 * b2 * G::kRowBytes;
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qt + off), kf[st], sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(gt + off), vf[st], dp, 0, 0, 0);
+      }
+      u32x4 pp[2], pd[2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float pr[2], ds[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = 2 * j + e;
+          const int lr = 32 * b2 + reg_key(i, h);  // row within the tile
+          const int row = r0 + lr;
+          bool vis = row < rhi;
+          if (branch_keys) vis = vis & (key >= m->rb[lr]) & (key <= row);
+          else vis = vis & (key < m->ra[lr]);
+          pr[e] = vis ? fast_exp2(fmaf(sc[i], p.c, -m->l2[lr])) : 0.f;
+          ds[e] = pr[e] * (dp[i] - m->dd[lr]);
+        }
+        pp[j >> 2][j & 3] = pack_bf16x2(pr[0], pr[1]);
+        pd[j >> 2][j & 3] = pack_bf16x2(ds[0], ds[1]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over these 32 rows
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const bf16x8 bp = __builtin_bit_cast(bf16x8, pp[c2]);
+        const bf16x8 bd = __builtin_bit_cast(bf16x8, pd[c2]);
+        const int rowb = (32 * b2 + 16 * c2) * G::kRowBytes;
+#pragma unroll
+        for (int md = 0; md < kDB; ++md) {
+          const s16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(gt + rowb + toff[md]));
+          const s16x4 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(gt + rowb + toff[kDB + md]));
+          const s16x4 gg[2] = {g0, g1};
+          dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, gg), bp, dv[md], 0, 0, 0);
+          const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(qt + rowb + toff[md]));
+          const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(qt + rowb + toff[kDB + md]));
+          const s16x4 qq[2] = {q0, q1};
+          dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qq), bd, dk[md], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  float4 ma, mb;
+  int4 mc, md4;
+  if (n_steps > 0) {
+    issue(0, lds0);
+    if (wave == 0) {
+      load_meta(0, ma, mb, mc, md4);
+      store_meta(lds0, ma, mb, mc, md4);
+    }
+  }
+  auto step = [&](int s, unsigned char* cur, unsigned char* nxt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies into cur are done
+    __syncthreads();                     // ... and every wave's; reads of nxt are retired
+    const bool more = s + 1 < n_steps;
+    if (more) {
+      issue(s + 1, nxt);
+      if (wave == 0) load_meta(s + 1, ma, mb, mc, md4);
+    }
+    consume(cur, s);
+    if (more && wave == 0) store_meta(nxt, ma, mb, mc, md4);
+  };
+#pragma unroll 1
+  for (int s = 0; s < n_steps; s += 2) {
+    step(s, lds0, lds1);
+    if (s + 1 < n_steps) step(s + 1, lds1, lds0);
+  }
+
+  if (!key_ok) return;
+  T* kd = reinterpret_cast<T*>(p.dk) + (int64_t(key) * p.hkv + kvh) * D;
+  T* vd = reinterpret_cast<T*>(p.dv) + (int64_t(key) * p.hkv + kvh) * D;
+#pragma unroll
+  for (int md = 0; md < kDB; ++md)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * md + 8 * g + 4 * h;
+      u32x2 a = {pack_bf16x2(dk[md][4 * g] * p.scale, dk[md][4 * g + 1] * p.scale),
+                 pack_bf16x2(dk[md][4 * g + 2] * p.scale, dk[md][4 * g + 3] * p.scale)};
+      u32x2 b = {pack_bf16x2(dv[md][4 * g], dv[md][4 * g + 1]), pack_bf16x2(dv[md][4 * g + 2], dv[md][4 * g + 3])};
+      *reinterpret_cast<u32x2*>(kd + d0) = a;
+      *reinterpret_cast<u32x2*>(vd + d0) = b;
+    }
+}
+
+template __global__ void bwd_prep_kernel<32>(BwdParams);
+template __global__ void bwd_prep_kernel<64>(BwdParams);
+template __global__ void bwd_prep_kernel<128>(BwdParams);
+#define TA_INSTANTIATE_BWD(D)                              \
+  template __global__ void bwd_dq_kernel<D, 1>(BwdParams); \
+  template __global__ void bwd_dq_kernel<D, 2>(BwdParams); \
+  template __global__ void bwd_dkdv_kernel<D>(BwdParams);
+TA_INSTANTIATE_BWD(32)
+TA_INSTANTIATE_BWD(64)
+TA_INSTANTIATE_BWD(128)
+#undef TA_INSTANTIATE_BWD
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdParams& p, int n_work, int n_kwork, hipStream_t st) {
+  const int64_t pairs = p.n_rows * p.hq;
+  if (pairs > 0) hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(unsigned((pairs + 3) / 4)), dim3(256), 0, st, p);
+  if (n_work > 0) {
+    if (p.group == 1)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 1>), dim3(unsigned(n_work) * unsigned(p.hkv), 1u), dim3(128), 0, st, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), dim3(unsigned(n_work) * unsigned(p.hkv), unsigned(p.group / 2)),
+                         dim3(256), 0, st, p);
+  }
+  if (n_kwork > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(unsigned(n_kwork) * unsigned(p.hkv)), dim3(128), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BwdParams& p, int n_work, int n_kwork, int d, hipStream_t st) {
+  if (d == 32) return launch_bwd_d<32>(p, n_work, n_kwork, st);
+  if (d == 64) return launch_bwd_d<64>(p, n_work, n_kwork, st);
+  if (d == 128) return launch_bwd_d<128>(p, n_work, n_kwork, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ta

@@ -76,6 +76,8 @@ void pack_blob(ta_plan* p) {
   off = align256(off + int64_t(p->row_mask.size() * 8));
   L.merge = off;
   off = align256(off + int64_t(p->merge.size() * sizeof(MergeRow)));
+  L.kwork = off;
+  off = align256(off + int64_t(p->kwork.size() * sizeof(WorkItem)));
   L.total = std::max<int64_t>(off, 256);
   p->layout = L;
   p->blob.assign(size_t(L.total), 0);
@@ -87,6 +89,7 @@ void pack_blob(ta_plan* p) {
   put(L.row_b, p->row_b.data(), p->row_b.size() * 4);
   put(L.mask, p->row_mask.data(), p->row_mask.size() * 8);
   put(L.merge, p->merge.data(), p->merge.size() * sizeof(MergeRow));
+  put(L.kwork, p->kwork.data(), p->kwork.size() * sizeof(WorkItem));
 }
 
 }  // namespace ta
@@ -189,9 +192,51 @@ extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* 
       // holding main rows is fully visible only below its first row.
       pl->work.push_back(make_item(base + t0, t1 - t0, base, a_full, a_hi, b_lo, b_hi, -1, 0));
     }
+
+    // key-major tiles for the backward: a main key j is seen by the main rows
+    // [j, M) and by the rows of every branch whose bound exceeds j (bounds
+    // grow with k, so those rows form a suffix of the page); a branch key j
+    // of Y_k by the rows [j, end of Y_k)
+    std::vector<int64_t> bound(static_cast<size_t>(N)), bstart(static_cast<size_t>(N)), blen(static_cast<size_t>(N));
+    {
+      int64_t aL = 0, aC = 0;
+      for (int32_t k = 0; k < N; ++k) {
+        aL += layout_len[r + k];
+        bound[k] = base + P + aL;
+        bstart[k] = base + M + aC;
+        blen[k] = content_len[r + k];
+        aC += content_len[r + k];
+      }
+    }
+    auto row_tiles = [](int64_t lo, int64_t hi) { return hi > lo ? (hi - lo + kKeyTile - 1) / kKeyTile : 0; };
+    for (int64_t k0 = base; k0 < base + M; k0 += kKeyTile) {
+      const int64_t k1 = std::min(base + M, k0 + kKeyTile);
+      int64_t first = base + T;  // first row of the first non-empty branch that sees key k0
+      for (int32_t k = 0; k < N; ++k)
+        if (bound[k] > k0 && blen[k] > 0) {
+          first = bstart[k];
+          break;
+        }
+      WorkItem w = make_item(k0, k1 - k0, k0, k0, base + M, first, base + T, -1, 0);
+      w.tile_lo = 0;
+      w.tile_hi = int32_t(row_tiles(k0, base + M) + row_tiles(first, base + T));
+      pl->kwork.push_back(w);
+    }
+    for (int64_t k0 = base + M; k0 < base + T; k0 += kKeyTile) {
+      const int64_t k1 = std::min(base + T, k0 + kKeyTile);
+      int64_t end = k1;  // end of the last branch with a key in [k0, k1)
+      for (int32_t k = 0; k < N; ++k)
+        if (bstart[k] < k1 && bstart[k] + blen[k] > k0) end = std::max(end, bstart[k] + blen[k]);
+      WorkItem w = make_item(k0, k1 - k0, k0, k0, end, 0, 0, -1, kKeyBranch);
+      w.tile_lo = 0;
+      w.tile_hi = int32_t(row_tiles(k0, end));
+      pl->kwork.push_back(w);
+    }
     base += T;
     r += N;
   }
+  std::stable_sort(pl->kwork.begin(), pl->kwork.end(),
+                   [](const WorkItem& x, const WorkItem& y) { return x.tile_hi > y.tile_hi; });
   for (int64_t i = 0; i < total_tokens; ++i) {
     pl->row_a[i] = int32_t(pl->main_end[i]);
     pl->row_b[i] = int32_t(pl->branch_start[i]);

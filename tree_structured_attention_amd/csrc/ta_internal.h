@@ -38,6 +38,15 @@ struct WorkItem {
 };
 static_assert(sizeof(WorkItem) == 48, "work item layout");
 constexpr int32_t kSegBFull = 1;
+// Key-major work items of the prefill backward (dK, dV) reuse WorkItem:
+//   keys  [row0, row0 + nrows) one 64-key tile of a page's main stream or
+//         of its branch area; flags bit 1 set for the branch area
+//   rows  [a_lo, a_hi) and [b_lo, b_hi): the query rows that can see a key
+//         of the tile (every pair is still tested per row against row_a /
+//         row_b: a main key is visible to rows with key < row_a, a branch
+//         key to rows with row_b <= key <= row)
+//   tile_hi  number of 64-row tiles walked (cost order)
+constexpr int32_t kKeyBranch = 2;
 
 // Merge table, one entry per output row combined from partials: slots are
 // sh_first + c * sh_stride (c < sh_count), then sf_first + c (c < sf_count),
@@ -50,7 +59,7 @@ static_assert(sizeof(MergeRow) == 32, "merge row layout");
 
 // Offsets (bytes) of the tables inside the device workspace.
 struct DeviceLayout {
-  int64_t work = 0, row_a = 0, row_b = 0, mask = 0, merge = 0, total = 0;
+  int64_t work = 0, row_a = 0, row_b = 0, mask = 0, merge = 0, kwork = 0, total = 0;
 };
 
 }  // namespace ta
@@ -71,6 +80,7 @@ struct ta_plan {
   std::vector<int32_t> row_a, row_b;
   std::vector<uint64_t> row_mask;
   std::vector<ta::MergeRow> merge;
+  std::vector<ta::WorkItem> kwork;  // prefill: key-major items of the backward
   ta::DeviceLayout layout;
   std::vector<unsigned char> blob;  // packed image of the device tables
 

@@ -41,7 +41,32 @@ struct MergeParams {
   int32_t hq;
 };
 
+// Backward of the packed prefill (bf16): gradients dq [rows, hq, d], dk and
+// dv [rows, hkv, d] from q, k, v, o, lse and dO.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* lse;  // [hq, rows] natural log, as the forward writes it
+  float* l2;         // scratch [hq, rows]: lse * log2(e)
+  float* dd;         // scratch [hq, rows]: sum_d dO * O
+  const WorkItem* work;   // row-major items (the forward's)
+  const WorkItem* kwork;  // key-major items
+  const int32_t* row_a;
+  const int32_t* row_b;
+  int32_t hq, hkv, group;
+  float c;      // scale * log2(e)
+  float scale;
+  int64_t n_rows;
+};
+
 hipError_t launch_attention(int mode, int dtype, const AttnParams& p, int n_work, int head_dim, hipStream_t st);
 hipError_t launch_merge(int dtype, const MergeParams& p, int head_dim, hipStream_t st);
+hipError_t launch_backward(const BwdParams& p, int n_work, int n_kwork, int head_dim, hipStream_t st);
 
 }  // namespace ta
