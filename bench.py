@@ -2,11 +2,14 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-One step is one pass of every entry point over resident synthetic inputs:
+One step is one pass of every forward entry point over resident synthetic
+inputs:
   prefill  one packed page: P = 4096, 24 regions of 12 layout tokens,
            lognormal content (8,772 tokens), 16q/8kv heads, d = 128, bf16
   decode   16 pages x 24 live branches, P = 4809, s_k ~ U{0..1024}
   verify   64 pages x 8 draft trees of 32 nodes, contexts ~ U{4096..16384}
+The prefill backward (dq, dk, dv of the same page) is timed in the same loop
+and reported under entries, outside the step.
 Each entry point is bracketed by HIP events on the stream it is launched on
 (torch's current stream).  The single JSON line on stdout reports prefill
 packed tokens/s as `value`, with decode and verify beside it, a roofline per
@@ -126,6 +129,33 @@ def verify_case():
                 flops=flops, bytes=bytes_, bound="mfma", plan_us=plan_us, kernel="attn_kernel<bf16,128,2,verify>")
 
 
+def backward_case():
+    """Prefill backward (dq, dk, dv) of the one-page workload: timed beside the
+    step, not inside it (the step is the forward hot path)."""
+    w = synth.config2()
+    plan = ta.plan_for(w.desc)  # the backward walks an unbalanced plan
+    plan.upload()
+    t = {k: v.cuda() for k, v in w.tensors.items()}
+    rng = np.random.default_rng(101)
+    g = torch.from_numpy(rng.standard_normal(tuple(t["q"].shape), dtype=np.float32)).to(torch.bfloat16).cuda()
+    o, lse = ta.prefill(plan, t["q"], t["k"], t["v"], scale=w.scale)
+    dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    need = ta.backward_scratch_bytes(plan, w.hq)
+    scratch = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    info = plan.info
+
+    def run():
+        ta.prefill_backward(plan, t["q"], t["k"], t["v"], o, lse, g, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                            scratch=scratch)
+
+    # dv = P^T dO, dP = dO V^T, dq = dS K, dk = dS^T Q: 4 products of 2 d flops
+    # per visible pair and query head (the recomputed S is not counted)
+    flops = 8.0 * w.head_dim * w.hq * info["visible_pairs"]
+    return dict(name="backward", w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="packed tokens",
+                flops=flops, bytes=None, bound="mfma", plan_us=0.0, in_step=False,
+                kernel="bwd_prep_kernel<128> + bwd_dq_kernel<128,2> + bwd_dkdv_kernel<128>")
+
+
 def traffic_for(kernel_name):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if
     they were taken on the current kernel source (else None)."""
@@ -179,7 +209,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "verify"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward"], default=None,
                     help="time one entry point only (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB three times "
@@ -203,7 +233,8 @@ def main():
         del src, dst
     log("[bench] generating inputs")
     cases = []
-    for name, fn in (("prefill", prefill_case), ("decode", decode_case), ("verify", verify_case)):
+    for name, fn in (("prefill", prefill_case), ("decode", decode_case), ("verify", verify_case),
+                     ("backward", backward_case)):
         if args.only is None or args.only == name:
             cases.append(fn())
             log(f"[bench] {name}: {cases[-1]['w'].name} ready")
@@ -248,8 +279,9 @@ def main():
         per_case[c["name"]] = r
         log(f"[bench] {c['name']}: {avg * 1e3:.1f} us  {json.dumps(r['roofline'])}")
 
-    step_ms = sum(per_case[c["name"]]["ms_avg"] for c in cases)
-    dominant = max(per_case, key=lambda k: per_case[k]["ms_avg"])
+    step_names = [c["name"] for c in cases if c.get("in_step", True)] or [c["name"] for c in cases]
+    step_ms = sum(per_case[n]["ms_avg"] for n in step_names)
+    dominant = max(step_names, key=lambda k: per_case[k]["ms_avg"])
     head = per_case.get("prefill") or per_case[dominant]
     value = head.get("packed_tokens_per_s") or next(v for k, v in head.items() if k.endswith("_per_s"))
     out = {
@@ -278,6 +310,8 @@ def main():
         out["decode_hbm_frac"] = per_case["decode"]["roofline"]["frac"]
     if "prefill" in per_case:
         out["prefill_mfma_frac"] = per_case["prefill"]["roofline"]["frac"]
+    if "backward" in per_case:
+        out["backward_mfma_frac"] = per_case["backward"]["roofline"]["frac"]
     if not args.no_cpu_baseline and args.only is None:
         log("[bench] timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)

@@ -11,6 +11,7 @@ from .tree_attn_oracle import (  # noqa: F401
     masked_attention_backward,
     prefill,
     prefill_backward,
+    prefill_backward_sampled,
     decode,
     verify,
     plan_prefill,

@@ -249,6 +249,47 @@ def prefill_backward(desc, q, k, v, do, scale: float):
     return dq, dk, dv
 
 
+def prefill_backward_sampled(desc, q, k, v, do, scale: float, rows, keys):
+    """dq of the packed rows ``rows`` and dk, dv of the packed tokens
+    ``keys``, from the same definition as ``prefill_backward`` but one row or
+    one key column at a time (for pages too large for the dense gradient).
+    Uses the fp64 forward (o, lse) of every page.  Returns dq [len(rows), Hq,
+    d], dk and dv [len(keys), Hkv, d]."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    o, lse = prefill(desc, q, k, v, scale)
+    dd = (do * o).sum(axis=2)  # [T, Hq]
+    rows, keys = [int(r) for r in rows], [int(j) for j in keys]
+    dq = np.zeros((len(rows), hq, d))
+    dk = np.zeros((len(keys), hkv, d))
+    dv = np.zeros((len(keys), hkv, d))
+    for p, P, L, C, base in _page_offsets(desc.prefix_len, desc.n_regions, desc.layout_len, desc.content_len):
+        tp = P + sum(L) + sum(C)
+        mine_r = [(n, r - base) for n, r in enumerate(rows) if base <= r < base + tp]
+        mine_k = [(n, j - base) for n, j in enumerate(keys) if base <= j < base + tp]
+        if not mine_r and not mine_k:
+            continue
+        sl = slice(base, base + tp)
+        mask = ancestor_mask_page(P, L, C)
+        qp, kp, vp, dop = q[sl], k[sl], v[sl], do[sl]
+        for h in range(hq):
+            kh, vh = kp[:, h // g, :], vp[:, h // g, :]
+            for n, i in mine_r:
+                s = np.where(mask[i], scale * (kh @ qp[i, h]), -np.inf)
+                pr = np.exp(s - lse[h, base + i])
+                ds = pr * (vh @ dop[i, h] - dd[base + i, h])
+                dq[n, h] = scale * (ds @ kh)
+            for n, j in mine_k:
+                s = np.where(mask[:, j], scale * (qp[:, h, :] @ kh[j]), -np.inf)
+                pr = np.exp(s - lse[h, sl])
+                ds = pr * (dop[:, h, :] @ vh[j] - dd[sl, h])
+                dk[n, h // g] += scale * (ds @ qp[:, h, :])
+                dv[n, h // g] += pr @ dop[:, h, :]
+    return dq, dk, dv
+
+
 def decode(desc, q, k_main, v_main, k_suffix, v_suffix, scale: float, rows=None):
     """One query token per live branch ([PaDoc] "Inference"; [HPD] shared prefix).
 

@@ -104,3 +104,36 @@ def test_backward_rejects_balanced_plan_and_fp32():
         with pytest.raises(ta.TreeAttnError) as e:
             ta.prefill_backward(bal, q, k, v, o, lse, do)
         assert e.value.code == ta.TA_ERR_STATE
+
+
+def test_backward_config2_full_size_sampled():
+    """The one-page prefill workload (P=4096, 24 regions, 8,772 tokens,
+    16q/8kv, d=128) in the launch configuration the bench times; dq checked on
+    sampled rows and dk, dv on sampled keys (main stream, layout units,
+    branch starts and ends), each computed by the oracle one at a time."""
+    w = synth.config2()
+    desc, t = w.desc, w.tensors
+    rng = np.random.default_rng(77)
+    g = torch.from_numpy(rng.standard_normal(tuple(t["q"].shape), dtype=np.float32)).to(torch.bfloat16)
+    say(f"[backward] config2 rows={desc.total_tokens()}")
+    dq, dk, dv = gpu_backward(desc, t, g, w.scale)
+    ref_plan = oracle.plan_prefill(desc)
+    T = desc.total_tokens()
+    M = int(ref_plan["pages"][0][1])
+    br = ref_plan["branches"]
+    picks = {0, 1, 63, 64, 1000, 4095, 4096, M - 1, M, T - 1}
+    for b in range(0, len(br), 5):
+        s0, n = int(br[b][1]), int(br[b][2])
+        if n:
+            picks |= {s0, s0 + n // 2, s0 + n - 1}
+    picks |= set(rng.integers(0, T, 12).tolist())
+    idx = sorted(picks)
+    rq, rk, rv = oracle.prefill_backward_sampled(desc, t["q"], t["k"], t["v"], g, w.scale, idx, idx)
+    # the tensors' scale is taken over the whole GPU result (the oracle only
+    # has the samples)
+    for got, ref, name in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        scale = float(np.abs(got).max())
+        err = np.abs(got[idx] - ref)
+        bad = err > 2e-2 * scale + 1e-2 * np.abs(ref)
+        assert not bad.any(), f"{name}: {bad.sum()} outside; max_abs={err.max():.3g} scale={scale:.3g}"
+        say(f"    {name}: {len(idx)} samples, max_abs/scale={err.max() / scale:.3g}")

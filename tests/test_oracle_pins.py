@@ -507,3 +507,21 @@ def test_backward_pages_and_unseen_keys_get_no_gradient():
     unseen = [6, 7, 11]  # B_2 and the second branch's content
     assert np.all(dk[unseen] == 0) and np.all(dv[unseen] == 0)
     assert np.all(np.abs(dv[[0, 1, 2, 3, 4, 5, 8, 9, 10]]).sum(axis=(1, 2)) > 0)
+
+
+def test_sampled_backward_equals_full_backward():
+    """The row/column-at-a-time oracle used on large pages equals the dense
+    one on pages small enough for both."""
+    rng = np.random.default_rng(14)
+    pages = [(9, [2, 0, 3], [5, 0, 4]), (4, [1], [6])]
+    desc = synth.make_prefill_desc([p[0] for p in pages], [np.array(p[1]) for p in pages],
+                                   [np.array(p[2]) for p in pages])
+    T = desc.total_tokens()
+    q, k, v, do = rand(rng, T, 4, 8), rand(rng, T, 2, 8), rand(rng, T, 2, 8), rand(rng, T, 4, 8)
+    dq, dk, dv = oracle.prefill_backward(desc, q, k, v, do, 0.4)
+    rows = [0, 5, 13, 20, 23, T - 1]
+    keys = [1, 9, 14, 18, 27, T - 2]
+    sq, sk, sv = oracle.prefill_backward_sampled(desc, q, k, v, do, 0.4, rows, keys)
+    assert np.max(np.abs(sq - dq[rows])) < 1e-12
+    assert np.max(np.abs(sk - dk[keys])) < 1e-12
+    assert np.max(np.abs(sv - dv[keys])) < 1e-12
