@@ -68,9 +68,10 @@ extern "C" {
 #define TA_FIELD_DECODE_ROWS 6  /* decode:  [branches][5] main_start, main_len, suffix_start, suffix_len, position */
 #define TA_FIELD_VERIFY_MASK 7  /* verify:  [nodes] ancestor bitmask (bit j: node j of the same branch is an ancestor or itself) */
 #define TA_FIELD_VERIFY_ROWS 8  /* verify:  [nodes][4] ctx_start, ctx_len, tree_base (abs node 0 of the branch), position */
-#define TA_FIELD_BWD_WORK 10    /* prefill: [items][10] key-major backward items, same columns as TA_FIELD_WORK:
-                                   keys [row0, row0 + nrows), rows [a_lo, a_hi) and [b_lo, b_hi), flags in a_full's
-                                   place is not exported; tile_hi = row tiles walked */
+#define TA_FIELD_BWD_WORK 10    /* prefill: [items][10] key-major backward items: key0, n_keys, a_lo, a_full, a_hi,
+                                   b_lo, b_hi, b_full, flags (2: branch-area keys), row tiles walked; rows
+                                   [a_lo, a_hi) and [b_lo, b_hi) can see the keys, rows from a_full / b_full on
+                                   see all of them */
 #define TA_FIELD_WORK 9         /* any:     [work][10] the launch work list: row0, nrows, a_lo, a_full, a_hi, b_lo, b_hi,
                                            partial slot (-1: direct), tile_lo, tile_hi (diagnostic; order is not contractual) */
 

@@ -67,13 +67,16 @@ def check_backward_items(desc, plan):
         keys = range(t) if t <= 2048 else range(0, t, 37)  # every key of small pages, a sample of large ones
         for j in keys:
             w = items[owner[base + j]]
-            k0, nk, flags = int(w[0]), int(w[1]), int(w[3])
+            k0, nk, flags = int(w[0]), int(w[1]), int(w[8])
             in_branch = base + j >= base + M
             assert bool(flags & 2) == in_branch
             assert (k0 >= base + M) == in_branch and (k0 + nk <= base + M or in_branch)
             rows = base + np.nonzero(mask[:, j])[0]
             seg = ((rows >= w[2]) & (rows < w[4])) | ((rows >= w[5]) & (rows < w[6]))
             assert seg.all(), (p, j)
+            # rows declared fully visible see this key
+            full = np.r_[np.arange(w[3], w[4]), np.arange(w[7], w[6])]
+            assert mask[full - base, j].all(), (p, j)
         base += t
 
 

@@ -153,8 +153,8 @@ extern "C" int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t
     case TA_FIELD_BWD_WORK:
       if (k != TA_PLAN_PREFILL) break;
       for (const WorkItem& w : plan->kwork)
-        work_tmp.insert(work_tmp.end(), {w.row0, w.nrows, w.a_lo, w.flags, w.a_hi, w.b_lo, w.b_hi, w.out,
-                                         w.tile_lo, w.tile_hi});
+        work_tmp.insert(work_tmp.end(), {w.row0, w.nrows, w.a_lo, w.a_full, w.a_hi, w.b_lo, w.b_hi, w.out,
+                                         w.flags, w.tile_hi});
       src = &work_tmp;
       break;
     case TA_FIELD_WORK:

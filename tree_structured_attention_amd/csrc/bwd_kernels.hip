@@ -147,6 +147,7 @@ __global__ __launch_bounds__(128 * GH, 2) void bwd_dq_kernel(BwdParams p) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kl + off), qf[st], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vl + off), df[st], dp, 0, 0, 0);
       }
+      sched_ld_mfma<0, 2 * kQSteps, 1, 4>();
       // dS^T = P^T (dP^T - Dd), P^T = 2^(s c - lse2); invisible pairs get 0
       u32x4 pk[2];
 #pragma unroll
@@ -180,6 +181,7 @@ __global__ __launch_bounds__(128 * GH, 2) void bwd_dq_kernel(BwdParams p) {
           acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb, acc[md], 0, 0, 0);
         }
       }
+      sched_ld_mfma<0, 2 * kDB, 2, 4>();
     }
   };
   auto step = [&](int it, const unsigned char* cur, unsigned char* nxt) {
@@ -328,6 +330,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const RowMeta* m = reinterpret_cast<const RowMeta*>(stage + G::kStageBytes);
     const int r = s % n_rt;
     const int r0 = rt0(r), rhi = rt_hi(r);
+    // row tiles past the segment's first fully visible row need no test
+    // (rows past the segment end hold zero Q, dO, lse2 and Dd: they add 0)
+    const bool masked = r0 < (r < n_a ? wi.a_full : wi.out);
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
       // S = Q K^T and dP = dO V^T for rows [32 b2, 32 b2 + 32) of the tile:
@@ -339,6 +344,35 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qt + off), kf[st], sc, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(gt + off), vf[st], dp, 0, 0, 0);
       }
+      sched_ld_mfma<0, 2 * kQSteps, 1, 4>();
+      // the lane's 16 rows are 32 b2 + reg_key(i, h): four runs of 4
+      // consecutive rows, read as float4 / int4
+      float l2v[16], ddv[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int lr = 32 * b2 + reg_key(4 * q4, h);
+        const float4 a = *reinterpret_cast<const float4*>(&m->l2[lr]);
+        const float4 d = *reinterpret_cast<const float4*>(&m->dd[lr]);
+        l2v[4 * q4] = a.x; l2v[4 * q4 + 1] = a.y; l2v[4 * q4 + 2] = a.z; l2v[4 * q4 + 3] = a.w;
+        ddv[4 * q4] = d.x; ddv[4 * q4 + 1] = d.y; ddv[4 * q4 + 2] = d.z; ddv[4 * q4 + 3] = d.w;
+      }
+      bool vis[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vis[i] = true;
+      if (masked) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int lr = 32 * b2 + reg_key(4 * q4, h);
+          const int4 ra4 = *reinterpret_cast<const int4*>(&m->ra[lr]);
+          const int4 rb4 = *reinterpret_cast<const int4*>(&m->rb[lr]);
+          const int ra[4] = {ra4.x, ra4.y, ra4.z, ra4.w}, rb[4] = {rb4.x, rb4.y, rb4.z, rb4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = r0 + lr + e;
+            vis[4 * q4 + e] = (row < rhi) & (branch_keys ? ((key >= rb[e]) & (key <= row)) : (key < ra[e]));
+          }
+        }
+      }
       u32x4 pp[2], pd[2];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -346,13 +380,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int i = 2 * j + e;
-          const int lr = 32 * b2 + reg_key(i, h);  // row within the tile
-          const int row = r0 + lr;
-          bool vis = row < rhi;
-          if (branch_keys) vis = vis & (key >= m->rb[lr]) & (key <= row);
-          else vis = vis & (key < m->ra[lr]);
-          pr[e] = vis ? fast_exp2(fmaf(sc[i], p.c, -m->l2[lr])) : 0.f;
-          ds[e] = pr[e] * (dp[i] - m->dd[lr]);
+          pr[e] = vis[i] ? fast_exp2(fmaf(sc[i], p.c, -l2v[i])) : 0.f;
+          ds[e] = pr[e] * (dp[i] - ddv[i]);
         }
         pp[j >> 2][j & 3] = pack_bf16x2(pr[0], pr[1]);
         pd[j >> 2][j & 3] = pack_bf16x2(ds[0], ds[1]);
@@ -375,6 +404,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qq), bd, dk[md], 0, 0, 0);
         }
       }
+      sched_ld_mfma<0, 4 * kDB, 2, 8>();
     }
   };
 

@@ -217,7 +217,15 @@ extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* 
           first = bstart[k];
           break;
         }
-      WorkItem w = make_item(k0, k1 - k0, k0, k0, base + M, first, base + T, -1, 0);
+      int64_t full_b = base + T;  // first row of the first non-empty branch that sees all of [k0, k1)
+      for (int32_t k = 0; k < N; ++k)
+        if (bound[k] >= k1 && blen[k] > 0) {
+          full_b = bstart[k];
+          break;
+        }
+      // main rows r >= k1 - 1 see every key of the tile; so do the rows of
+      // every branch from full_b on
+      WorkItem w = make_item(k0, k1 - k0, k0, k1 - 1, base + M, first, base + T, std::max(full_b, first), 0);
       w.tile_lo = 0;
       w.tile_hi = int32_t(row_tiles(k0, base + M) + row_tiles(first, base + T));
       pl->kwork.push_back(w);
@@ -227,7 +235,7 @@ extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* 
       int64_t end = k1;  // end of the last branch with a key in [k0, k1)
       for (int32_t k = 0; k < N; ++k)
         if (bstart[k] < k1 && bstart[k] + blen[k] > k0) end = std::max(end, bstart[k] + blen[k]);
-      WorkItem w = make_item(k0, k1 - k0, k0, k0, end, 0, 0, -1, kKeyBranch);
+      WorkItem w = make_item(k0, k1 - k0, k0, end, end, 0, 0, 0, kKeyBranch);
       w.tile_lo = 0;
       w.tile_hi = int32_t(row_tiles(k0, end));
       pl->kwork.push_back(w);

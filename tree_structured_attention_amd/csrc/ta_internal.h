@@ -42,9 +42,10 @@ constexpr int32_t kSegBFull = 1;
 //   keys  [row0, row0 + nrows) one 64-key tile of a page's main stream or
 //         of its branch area; flags bit 1 set for the branch area
 //   rows  [a_lo, a_hi) and [b_lo, b_hi): the query rows that can see a key
-//         of the tile (every pair is still tested per row against row_a /
-//         row_b: a main key is visible to rows with key < row_a, a branch
-//         key to rows with row_b <= key <= row)
+//         of the tile; rows from a_full (segment A) and from `out` (segment
+//         B) on see every key of it.  Other row tiles are tested per row
+//         against row_a / row_b: a main key is visible to rows with
+//         key < row_a, a branch key to rows with row_b <= key <= row
 //   tile_hi  number of 64-row tiles walked (cost order)
 constexpr int32_t kKeyBranch = 2;
 
