@@ -21,3 +21,10 @@ from .tree_attn_oracle import (  # noqa: F401
     tree_ancestor_mask,
     lse_merge,
 )
+from .draft_oracle import (  # noqa: F401,E402
+    draft_candidates,
+    prefix_tree,
+    draft_tree,
+    tree_accept,
+    chain_accept,
+)
