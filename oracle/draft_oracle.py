@@ -32,6 +32,7 @@ Readings where the notes are silent (listed in the design notes):
     hang off the accepted sequence);
   * a node budget caps the tree: insertion stops at the first token that
     would create a node beyond it (earlier candidates keep their nodes);
+    an optional depth budget first cuts every candidate to that many tokens;
   * ties in "highest" go to the lowest node index (children) and the lowest
     token id (vocabulary).
 """
@@ -57,12 +58,17 @@ def draft_candidates(accepted, drafts, window: int = 3):
     return out
 
 
-def prefix_tree(candidates, max_nodes: int):
-    """Linearised prefix tree of the candidates: (tokens, parent) lists."""
+def prefix_tree(candidates, max_nodes: int, max_depth=None):
+    """Linearised prefix tree of the candidates: (tokens, parent) lists.
+
+    max_depth (optional) keeps only the first max_depth tokens of each
+    candidate."""
     tokens, parent = [], []
     children = {-1: {}}  # node -> {token: child node}
     for cand in candidates:
         cur = -1
+        if max_depth is not None:
+            cand = cand[:max_depth]
         for t in cand:
             t = int(t)
             nxt = children[cur].get(t)
@@ -81,9 +87,9 @@ def prefix_tree(candidates, max_nodes: int):
     return tokens, parent
 
 
-def draft_tree(accepted, drafts, window: int = 3, max_nodes: int = 64):
+def draft_tree(accepted, drafts, window: int = 3, max_nodes: int = 64, max_depth=None):
     """Window match, then prefix tree ([HSD] key design 3 (a) + (b))."""
-    return prefix_tree(draft_candidates(accepted, drafts, window), max_nodes)
+    return prefix_tree(draft_candidates(accepted, drafts, window), max_nodes, max_depth)
 
 
 def tree_accept(tokens, parent, logp, tau: float = 0.75, exact: bool = False):

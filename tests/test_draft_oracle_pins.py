@@ -46,6 +46,8 @@ def test_golden_draft_tree_round():
     assert tok == ints(fx["tokens"][0]) and par == ints(fx["parent"][0])
     tok5, par5 = oracle.draft_tree(accepted, drafts, n, max_nodes=5)
     assert tok5 == ints(fx["tokens_cap5"][0]) and par5 == ints(fx["parent_cap5"][0])
+    tok2, par2 = oracle.draft_tree(accepted, drafts, n, max_nodes=64, max_depth=2)
+    assert tok2 == ints(fx["tokens_depth2"][0]) and par2 == ints(fx["parent_depth2"][0])
 
     V = int(fx["vocab"][0][0])
     logp = np.full((len(tok) + 1, V), -10.0)
@@ -115,10 +117,13 @@ def test_prefix_tree_is_the_set_of_distinct_prefixes():
         cands = [rng.integers(0, 3, int(rng.integers(1, 7))).tolist()
                  for _ in range(int(rng.integers(0, 6)))]
         cap = int(rng.integers(0, 40))
-        tok, par = oracle.prefix_tree(cands, cap)
+        depth = int(rng.integers(1, 8)) if trial % 2 else None
+        tok, par = oracle.prefix_tree(cands, cap, depth)
         pref = [_prefix_of(tok, par, i) for i in range(len(tok))]
-        # nodes are the first `cap` distinct prefixes in enumeration order
-        assert pref == _distinct_prefixes(cands)[:cap], trial
+        # nodes are the first `cap` distinct prefixes of length <= depth, in
+        # enumeration order
+        want = [p for p in _distinct_prefixes(cands) if depth is None or len(p) <= depth]
+        assert pref == want[:cap], trial
         assert all(-1 <= par[i] < i for i in range(len(par)))
         # the tree ancestor mask is the prefix relation
         a = oracle.tree_ancestor_mask(par) if tok else np.zeros((0, 0), bool)
