@@ -34,7 +34,8 @@ Readings where the notes are silent (listed in the design notes):
     would create a node beyond it (earlier candidates keep their nodes);
     an optional depth budget first cuts every candidate to that many tokens;
   * ties in "highest" go to the lowest node index (children) and the lowest
-    token id (vocabulary).
+    token id (vocabulary);
+  * a node whose token lies outside the vocabulary is never accepted.
 """
 from __future__ import annotations
 
@@ -105,11 +106,12 @@ def tree_accept(tokens, parent, logp, tau: float = 0.75, exact: bool = False):
     Returns (accepted node path, free token u_hat of the row after the path).
     """
     logp = np.asarray(logp)
-    n = len(tokens)
+    n, V = len(tokens), logp.shape[1]
     kids = {-1: []}
     for i in range(n):
         kids.setdefault(i, [])
-        kids[int(parent[i])].append(i)
+        if 0 <= int(tokens[i]) < V:  # a token outside the vocabulary is never a candidate
+            kids[int(parent[i])].append(i)
     log_tau = math.log(tau)
     path, cur, row = [], -1, 0
     while kids.get(cur):
