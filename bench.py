@@ -8,8 +8,9 @@ inputs:
            lognormal content (8,772 tokens), 16q/8kv heads, d = 128, bf16
   decode   16 pages x 24 live branches, P = 4809, s_k ~ U{0..1024}
   verify   64 pages x 8 draft trees of 32 nodes, contexts ~ U{4096..16384}
-The prefill backward (dq, dk, dv of the same page) is timed in the same loop
-and reported under entries, outside the step.
+The prefill backward (dq, dk, dv of the same page) and the greedy acceptance
+walk over the verify trees (bf16 logits, 151,936-entry vocabulary) are timed
+in the same loop and reported under entries, outside the step.
 Each entry point is bracketed by HIP events on the stream it is launched on
 (torch's current stream).  The single JSON line on stdout reports prefill
 packed tokens/s as `value`, with decode and verify beside it, a roofline per
@@ -156,6 +157,47 @@ def backward_case():
                 kernel="bwd_prep_kernel<128> + bwd_dq_kernel<128,2> + bwd_dkdv_kernel<128>")
 
 
+def accept_case():
+    """Greedy acceptance over the verify workload's draft trees (64 pages x 8
+    branches x 32 nodes) from bf16 logits over a 151,936-entry vocabulary:
+    timed beside the step, not inside it.  The host part (window match and
+    prefix-tree build from page-shaped drafts, then the verify plan) is timed
+    on the CPU and reported as its plan time."""
+    w = synth.config5(with_tensors=False)
+    desc = w.desc
+    vocab = synth.VOCAB
+    rng = np.random.default_rng(21)
+    # host: one tree per branch from 6 region drafts of 100-800 tokens whose
+    # last accepted tokens occur in them
+    drafts = [[rng.integers(0, vocab, int(rng.integers(100, 800))).tolist() for _ in range(6)] for _ in range(8)]
+    t0 = time.perf_counter()
+    for b in range(desc.n_branches):
+        ds = drafts[b % 8]
+        src = ds[b % 6]
+        cut = 3 + (b * 37) % (len(src) - 3)
+        ta.draft_tree(src[:cut], ds, 3, 32, 8)
+    plan = ta.plan_for(desc)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    plan.upload()
+    tokens = torch.as_tensor(synth.draft_tokens(rng, desc, vocab), device="cuda")
+    logits = synth.accept_logits(22, desc, tokens.cpu().numpy(), vocab, vocab, torch.bfloat16, "cuda")
+    n_trees = desc.n_branches
+    path = torch.empty(desc.total_nodes(), dtype=torch.int32, device="cuda")
+    n_path = torch.empty(n_trees, dtype=torch.int32, device="cuda")
+    nxt = torch.empty(n_trees, dtype=torch.int32, device="cuda")
+    scratch = torch.empty(ta.accept_scratch_bytes(plan, vocab) + 256, dtype=torch.uint8, device="cuda")
+
+    def run():
+        ta.accept(plan, logits, tokens, tau=0.75, path=path, n_path=n_path, next_token=nxt, scratch=scratch)
+
+    # every logits row is read once; the tree tables, tokens and results are
+    # a few hundred KB and left out
+    bytes_ = float(logits.numel() * 2)
+    return dict(name="accept", w=w, plan=plan, run=run, unit_count=n_trees, unit="draft trees",
+                flops=0.0, bytes=bytes_, bound="hbm", plan_us=plan_us, in_step=False,
+                kernel="row_argmax_kernel<bf16> + tree_walk_kernel<bf16>")
+
+
 def traffic_for(kernel_name):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if
     they were taken on the current kernel source (else None)."""
@@ -209,7 +251,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward", "accept"], default=None,
                     help="time one entry point only (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB three times "
@@ -234,7 +276,7 @@ def main():
     log("[bench] generating inputs")
     cases = []
     for name, fn in (("prefill", prefill_case), ("decode", decode_case), ("verify", verify_case),
-                     ("backward", backward_case)):
+                     ("backward", backward_case), ("accept", accept_case)):
         if args.only is None or args.only == name:
             cases.append(fn())
             log(f"[bench] {name}: {cases[-1]['w'].name} ready")
@@ -312,6 +354,8 @@ def main():
         out["prefill_mfma_frac"] = per_case["prefill"]["roofline"]["frac"]
     if "backward" in per_case:
         out["backward_mfma_frac"] = per_case["backward"]["roofline"]["frac"]
+    if "accept" in per_case:
+        out["accept_hbm_frac"] = per_case["accept"]["roofline"]["frac"]
     if not args.no_cpu_baseline and args.only is None:
         log("[bench] timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)

@@ -55,6 +55,9 @@ extern "C" {
 #define TA_DTYPE_F32 0
 #define TA_DTYPE_BF16 1
 
+#define TA_ACCEPT_TAU 0   /* greedy tree walk with the log tau test */
+#define TA_ACCEPT_EXACT 1 /* accept a drafted token only if it is the target's top token */
+
 #define TA_PLAN_PREFILL 1
 #define TA_PLAN_DECODE 2
 #define TA_PLAN_VERIFY 3
@@ -237,6 +240,81 @@ int tree_attn_verify(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv
                      const void* v_ctx, const void* k_tree, const void* v_tree,
                      void* o, float* lse, void* scratch, size_t scratch_bytes,
                      void* stream);
+
+/*
+ * Draft tree from decoupled drafts, on the host ("HSD: Training-Free
+ * Acceleration for Document Parsing Vision-Language Models with Hierarchical
+ * Speculative Decoding" notes, key design 3 (a) draft-target matching and
+ * (b) prefix-tree batching).
+ *   accepted[n_accepted]   tokens accepted so far; the last `window` of them
+ *                          (window >= 1; 3 in the notes) are the reference
+ *                          window w.  With fewer than `window` accepted
+ *                          tokens there is no candidate.
+ *   drafts, draft_len[n_drafts]  the drafts, concatenated.  Every position j
+ *                          of every draft where draft[j, j + window) == w
+ *                          yields the candidate draft[j + window, end);
+ *                          empty candidates are dropped.  Candidates are taken
+ *                          draft by draft, matches in position order.
+ *   max_depth              if > 0, each candidate is cut to its first
+ *                          max_depth tokens; 0 = no depth budget
+ *   max_nodes              node budget: insertion stops at the first token
+ *                          that would create node number max_nodes + 1
+ *                          (earlier nodes stay)
+ *   tokens[max_nodes], parent[max_nodes], *n_nodes  the prefix tree: one node
+ *                          per distinct candidate prefix, in creation order;
+ *                          parent -1 for nodes that follow the accepted
+ *                          sequence directly, else an earlier node.  This is
+ *                          the parent-array form tree_attn_plan_verify takes
+ *                          (which allows up to 64 nodes per tree).
+ * All pointers are host memory, owned by the caller.  Errors: INVALID_ARG for
+ * NULL arrays with a nonzero count, negative counts or budgets, window < 1;
+ * outputs untouched on error.
+ */
+int tree_attn_draft_tree(const int32_t* accepted, int32_t n_accepted, const int32_t* drafts,
+                         const int32_t* draft_len, int32_t n_drafts, int32_t window, int32_t max_nodes,
+                         int32_t max_depth, int32_t* tokens, int32_t* parent, int32_t* n_nodes);
+
+/* Device scratch (bytes) tree_attn_accept needs for a verify plan and a
+ * vocabulary of `vocab` entries (1 <= vocab < 2^31). */
+int tree_attn_accept_scratch_bytes(const ta_plan* plan, int64_t vocab, size_t* bytes);
+
+/*
+ * Greedy acceptance over the trees of an uploaded verify plan, from the
+ * target model's logits (HSD notes, key design 3, greedy tree traversal;
+ * HPD-Parsing notes, Algorithm 1, acceptance length n_acc).
+ *   logits   device, [sum over trees of (n_nodes + 1), ld] bf16 or fp32
+ *            (dtype), tree-major: row 0 of a tree scores the next token after
+ *            the accepted sequence, row 1 + i the token after node i.  Only
+ *            entries [0, vocab) of a row are read.  Log-probabilities or raw
+ *            logits give the same result (the test uses differences within a
+ *            row).  Aligned to the element size; NaN entries are not
+ *            supported.
+ *   tokens   device, [n_nodes] drafted token of each node (the plan's node
+ *            order); a node whose token is outside [0, vocab) is never
+ *            accepted.
+ *   mode     TA_ACCEPT_TAU: from the root, take the child u* with the highest
+ *            logit (ties: lowest node index) and accept it iff
+ *            z(u*) - z(u_hat) >= log(tau), in fp64, u_hat being the row's top
+ *            token (ties: lowest token id); stop at the first rejection or
+ *            at a leaf.  tau > 0 (0.75 in the notes).
+ *            TA_ACCEPT_EXACT: accept the child whose token is u_hat (lowest
+ *            node index if several); on a chain this is n_acc = max{k : the
+ *            target's greedy token equals drafted token i for all i <= k}.
+ *            tau is ignored.
+ *   path     device, [n_nodes]: tree b writes the accepted node indices
+ *            (local to the tree, root to tip) at [node_off_b, node_off_b +
+ *            n_path[b]); the rest is left untouched
+ *   n_path, next_token  device, [n_trees]: accepted count and the free token
+ *            u_hat of the row the walk ends on (the token to append after
+ *            the accepted path)
+ *   scratch  device, >= tree_attn_accept_scratch_bytes, 256-byte aligned
+ * Errors: STATE for a plan that is not a verify plan or not uploaded;
+ * INVALID_ARG for bad pointers, vocab, ld < vocab, tau or mode; WORKSPACE for
+ * missing or short scratch; CAPACITY when rows x argmax pieces reach 2^24.
+ */
+int tree_attn_accept(const ta_plan* plan, int32_t dtype, const void* logits, int64_t vocab, int64_t ld,
+                     const int32_t* tokens, double tau, int32_t mode, int32_t* path, int32_t* n_path,
+                     int32_t* next_token, void* scratch, size_t scratch_bytes, void* stream);
 
 /* Message of the last error on this thread ("" if none). */
 const char* tree_attn_last_error(void);

@@ -1,0 +1,182 @@
+"""GPU parity of tree_attn_accept against the oracle's greedy tree walk
+(HSD notes, key design 3; HPD-Parsing notes, Algorithm 1).  Index work, so
+the bar is bit-exact: the accepted node path, its length and the free token
+of every tree.  Both sides take the acceptance decision in fp64 on the same
+stored logits (bf16 or fp32)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tree_structured_attention_amd import binding as ta
+from tree_structured_attention_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def make_desc(rng, sizes, ctx=16, chains=False):
+    parents = []
+    for n in sizes:
+        if chains:
+            parents.append(np.arange(-1, n - 1, dtype=np.int32))
+        else:
+            par = np.full(n, -1, np.int32)
+            for i in range(1, n):
+                par[i] = int(rng.integers(-1, i))
+            parents.append(par)
+    n_b = len(sizes)
+    return synth.VerifyDesc(np.array([ctx], np.int32), np.zeros(n_b, np.int32), np.array(sizes, np.int32),
+                            np.concatenate(parents).astype(np.int32) if n_b else np.zeros(0, np.int32))
+
+
+def run_accept(desc, tokens, logits, vocab, tau, exact):
+    plan = ta.plan_for(desc).upload(DEV)
+    tok = torch.as_tensor(tokens, dtype=torch.int32, device=DEV)
+    n_nodes = desc.total_nodes()
+    path = torch.full((max(n_nodes, 1),), -5, dtype=torch.int32, device=DEV)
+    out = ta.accept(plan, logits, tok, tau=tau, exact=exact, vocab=vocab, path=path)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+def check_against_oracle(desc, tokens, logits, vocab, tau, exact, trees=None):
+    path, n_path, nxt = run_accept(desc, tokens, logits, vocab, tau, exact)
+    z = logits.float().cpu().numpy()[:, :vocab]
+    off = np.concatenate([[0], np.cumsum(desc.n_nodes.astype(np.int64))])
+    trees = range(desc.n_branches) if trees is None else trees
+    for b in trees:
+        n = int(desc.n_nodes[b])
+        lo = int(off[b])
+        want_path, want_free = oracle.tree_accept(tokens[lo:lo + n], desc.parent[lo:lo + n],
+                                                  z[lo + b:lo + b + n + 1], tau=tau, exact=exact)
+        got = path[lo:lo + n_path[b]].tolist()
+        assert (got, int(nxt[b])) == (want_path, want_free), (b, got, want_path, int(nxt[b]), want_free)
+        # entries past the accepted path are left as they were
+        assert (path[lo + n_path[b]:lo + n] == -5).all()
+    return n_path
+
+
+CASES = [
+    # (tree sizes, vocab, ld)
+    ([5, 0, 64, 1, 17], 7, 7),
+    ([5, 0, 64, 1, 17], 1000, 1000),
+    ([3, 30, 12], 12345, 12351),      # odd row stride: rows start off 16-byte boundaries
+    ([64] * 9, 40000, 40000),         # several argmax pieces per row
+    ([], 100, 100),
+    ([0, 0], 100, 100),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("mode", ["tau0.75", "tau0.5", "tau1", "exact"])
+def test_accept_matches_oracle(dtype, case, mode):
+    sizes, vocab, ld = CASES[case]
+    rng = np.random.default_rng(17 + case)
+    desc = make_desc(rng, sizes)
+    tokens = synth.draft_tokens(rng, desc, vocab)
+    logits = synth.accept_logits(5 + case, desc, tokens, vocab, ld, dtype, DEV)
+    tau = 0.75 if mode == "exact" else float(mode[3:])
+    print(f"accept case={case} sizes={sizes} vocab={vocab} ld={ld} {dtype} {mode}", flush=True)
+    check_against_oracle(desc, tokens, logits, vocab, tau, mode == "exact")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_accept_ties(dtype):
+    """Integer logits in a small range: many equal maxima and equal children,
+    so the tie rules (lowest token id for the top, lowest node index among
+    children) decide."""
+    rng = np.random.default_rng(3)
+    desc = make_desc(rng, [20, 33, 64, 8])
+    vocab = 50
+    tokens = rng.integers(0, 12, desc.total_nodes()).astype(np.int32)
+    rows = desc.total_nodes() + desc.n_branches
+    z = torch.as_tensor(rng.integers(-2, 3, (rows, vocab)), dtype=dtype, device=DEV)
+    for tau in (0.75, 1.0, 1e-3):
+        check_against_oracle(desc, tokens, z, vocab, tau, False)
+    check_against_oracle(desc, tokens, z, vocab, 1.0, True)
+
+
+def test_accept_out_of_vocabulary_tokens_are_never_accepted():
+    rng = np.random.default_rng(4)
+    desc = make_desc(rng, [16, 16, 16])
+    vocab = 300
+    tokens = synth.draft_tokens(rng, desc, vocab)
+    logits = synth.accept_logits(9, desc, tokens, vocab, 320, torch.bfloat16, DEV)
+    bad = rng.random(len(tokens)) < 0.3
+    tokens[bad] = rng.choice([-1, vocab, vocab + 5, 2 ** 31 - 1], int(bad.sum()))
+    for exact in (False, True):
+        check_against_oracle(desc, tokens, logits, vocab, 0.75, exact)
+
+
+def test_accept_chains_give_the_acceptance_length():
+    """HPD-Parsing's n_acc on drafted chains: exact mode on chain trees."""
+    rng = np.random.default_rng(6)
+    sizes = [int(x) for x in rng.integers(0, 12, 40)]
+    desc = make_desc(rng, sizes, chains=True)
+    vocab = 5000
+    tokens = synth.draft_tokens(rng, desc, vocab)
+    logits = synth.accept_logits(8, desc, tokens, vocab, vocab, torch.bfloat16, DEV)
+    path, n_path, nxt = run_accept(desc, tokens, logits, vocab, 0.75, True)
+    z = logits.float().cpu().numpy()
+    off = 0
+    for b, n in enumerate(sizes):
+        target = [int(np.argmax(z[off + b + i])) for i in range(n + 1)]
+        assert (int(n_path[b]), int(nxt[b])) == oracle.chain_accept(tokens[off:off + n], target)
+        assert path[off:off + n_path[b]].tolist() == list(range(int(n_path[b])))
+        off += n
+
+
+def test_accept_repeatable_and_independent_of_scratch_contents():
+    rng = np.random.default_rng(10)
+    desc = make_desc(rng, [32] * 16)
+    vocab = 32000
+    tokens = synth.draft_tokens(rng, desc, vocab)
+    logits = synth.accept_logits(11, desc, tokens, vocab, vocab, torch.bfloat16, DEV)
+    plan = ta.plan_for(desc).upload(DEV)
+    tok = torch.as_tensor(tokens, device=DEV)
+    need = ta.accept_scratch_bytes(plan, vocab)
+    outs = []
+    for fill in (0, 255, 7):
+        scratch = torch.full((need + 256,), fill, dtype=torch.uint8, device=DEV)
+        path = torch.full((desc.total_nodes(),), -5, dtype=torch.int32, device=DEV)
+        outs.append([t.cpu() for t in ta.accept(plan, logits, tok, path=path, scratch=scratch)])
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
+
+
+def test_accept_full_size_sampled():
+    """The verify workload's trees (64 pages x 8 branches x 32 nodes) over a
+    151,936-entry bf16 vocabulary, in the launch configuration the bench
+    times; 48 trees are checked against the oracle, every tree for validity."""
+    w = synth.config5(with_tensors=False)
+    desc = w.desc
+    vocab = synth.VOCAB
+    rng = np.random.default_rng(12)
+    tokens = synth.draft_tokens(rng, desc, vocab)
+    logits = synth.accept_logits(13, desc, tokens, vocab, vocab, torch.bfloat16, DEV)
+    sample = sorted(rng.choice(desc.n_branches, 48, replace=False).tolist())
+    path, n_path, nxt = run_accept(desc, tokens, logits, vocab, 0.75, False)
+    # validity for every tree: a root-to-tip chain whose top token is the free token's row top
+    off = np.concatenate([[0], np.cumsum(desc.n_nodes.astype(np.int64))])
+    for b in range(desc.n_branches):
+        lo, n = int(off[b]), int(desc.n_nodes[b])
+        p = path[lo:lo + n_path[b]].tolist()
+        cur = -1
+        for node in p:
+            assert 0 <= node < n and desc.parent[lo + node] == cur
+            cur = node
+        assert 0 <= nxt[b] < vocab
+    assert n_path.mean() > 1.0  # the planted logits give multi-token walks
+    # exact parity on the sampled trees
+    z_rows = []
+    for b in sample:
+        lo, n = int(off[b]), int(desc.n_nodes[b])
+        z = logits[lo + b:lo + b + n + 1].float().cpu().numpy()
+        want = oracle.tree_accept(tokens[lo:lo + n], desc.parent[lo:lo + n], z, 0.75)
+        assert (path[lo:lo + n_path[b]].tolist(), int(nxt[b])) == want, b
+        z_rows.append(z)
+    del z_rows

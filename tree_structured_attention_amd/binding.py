@@ -113,6 +113,11 @@ def lib() -> ctypes.CDLL:
             "tree_attn_backward_scratch_bytes": ([_P, i32, ctypes.POINTER(sz)], ctypes.c_int),
             "tree_attn_prefill_backward": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz,
                                             _P], ctypes.c_int),
+            "tree_attn_draft_tree": ([_I32P, i32, _I32P, _I32P, i32, i32, i32, i32, _I32P, _I32P, _I32P],
+                                     ctypes.c_int),
+            "tree_attn_accept_scratch_bytes": ([_P, i64, ctypes.POINTER(sz)], ctypes.c_int),
+            "tree_attn_accept": ([_P, i32, _P, i64, i64, _P, ctypes.c_double, i32, _P, _P, _P, _P, sz, _P],
+                                 ctypes.c_int),
             "tree_attn_last_error": ([], ctypes.c_char_p),
             "tree_attn_version": ([], ctypes.c_char_p),
         }
@@ -397,3 +402,72 @@ def prefill_backward(plan: Plan, q, k, v, o, lse, d_o, scale=None, dq=None, dk=N
                                             _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv), sp, sn,
                                             _stream_handle(stream)))
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# draft trees
+# ---------------------------------------------------------------------------
+
+TA_ACCEPT_TAU = 0
+TA_ACCEPT_EXACT = 1
+
+
+def draft_tree(accepted, drafts, window: int = 3, max_nodes: int = 64, max_depth: int = 0):
+    """Prefix tree of the draft continuations that follow the last `window`
+    accepted tokens.  Returns (tokens, parent) int32 arrays; parent -1 marks
+    nodes that follow the accepted sequence."""
+    acc = _i32(accepted)
+    ds = [_i32(d) for d in drafts]
+    lens = _i32([len(d) for d in ds])
+    cat = np.concatenate(ds) if ds else np.zeros(0, np.int32)
+    cat = _i32(cat)
+    tok = np.zeros(max(max_nodes, 0), np.int32)
+    par = np.zeros(max(max_nodes, 0), np.int32)
+    n = ctypes.c_int32()
+    _check(lib().tree_attn_draft_tree(_ptr(acc), acc.size, _ptr(cat), _ptr(lens), lens.size, window, max_nodes,
+                                      max_depth, _ptr(tok), _ptr(par), ctypes.byref(n)))
+    return tok[:n.value].copy(), par[:n.value].copy()
+
+
+def accept_scratch_bytes(plan: Plan, vocab: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().tree_attn_accept_scratch_bytes(plan.handle, vocab, ctypes.byref(n)))
+    return int(n.value)
+
+
+def accept(plan: Plan, logits, tokens, tau: float = 0.75, exact: bool = False, vocab: int = None,
+           path=None, n_path=None, next_token=None, scratch: Optional[torch.Tensor] = None, stream=None):
+    """Greedy acceptance over the trees of a verify plan.
+
+    logits: [n_nodes + n_trees, ld] bf16/fp32 on the GPU, tree-major (row 0 of
+    a tree scores the token after the accepted sequence, row 1 + i the token
+    after node i); tokens: int32 [n_nodes].  Returns (path, n_path,
+    next_token) int32 tensors: tree b's accepted nodes are
+    path[node_off[b] : node_off[b] + n_path[b]]."""
+    if logits.dim() != 2:
+        raise TreeAttnError(TA_ERR_INVALID_ARG, "logits is [rows, ld]")
+    ld = logits.shape[1]
+    vocab = ld if vocab is None else int(vocab)
+    info = plan_info(plan)
+    n_nodes, n_trees = info["n_rows"], info["n_branches"]
+    if logits.shape[0] < n_nodes + n_trees:
+        raise TreeAttnError(TA_ERR_INVALID_ARG, "logits needs n_nodes + n_trees rows")
+    if tokens.dtype != torch.int32 or tokens.numel() < n_nodes:
+        raise TreeAttnError(TA_ERR_INVALID_ARG, "tokens must be int32 with one entry per node")
+    for name, t, n in (("path", path, n_nodes), ("n_path", n_path, n_trees), ("next_token", next_token, n_trees)):
+        if t is not None and (t.dtype != torch.int32 or t.numel() < n):
+            raise TreeAttnError(TA_ERR_INVALID_ARG, f"{name} must be int32 with at least {n} entries")
+    dev = logits.device
+    path = torch.zeros(max(n_nodes, 1), dtype=torch.int32, device=dev) if path is None else path
+    n_path = torch.empty(max(n_trees, 1), dtype=torch.int32, device=dev) if n_path is None else n_path
+    next_token = torch.empty(max(n_trees, 1), dtype=torch.int32, device=dev) if next_token is None else next_token
+    need = accept_scratch_bytes(plan, vocab)
+    if scratch is None:
+        scratch = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    off = (-scratch.data_ptr()) % 256
+    view = scratch[off:]
+    _check(lib().tree_attn_accept(plan.handle, _dtype_code(logits), _dev_ptr(logits), vocab, ld, _dev_ptr(tokens),
+                                  float(tau), TA_ACCEPT_EXACT if exact else TA_ACCEPT_TAU, _dev_ptr(path),
+                                  _dev_ptr(n_path), _dev_ptr(next_token), ctypes.c_void_p(view.data_ptr()),
+                                  view.numel(), _stream_handle(stream)))
+    return path[:n_nodes], n_path[:n_trees], next_token[:n_trees]

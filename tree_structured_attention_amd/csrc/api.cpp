@@ -3,6 +3,8 @@
 // call leaves outputs and the stream untouched.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -356,4 +358,90 @@ extern "C" int tree_attn_prefill_backward(const ta_plan* plan, int32_t dtype, in
   return hip_status(launch_backward(p, int(plan->work.size()), int(plan->kwork.size()), head_dim,
                                     static_cast<hipStream_t>(stream)),
                     "prefill_backward launch");
+}
+
+namespace ta {
+namespace {
+
+// Argmax pieces per logits row: enough workgroups to fill the chip (about
+// eight per compute unit) without cutting a row below 8192 entries.
+constexpr int64_t kAcceptTargetBlocks = 2048;
+constexpr int64_t kAcceptMinChunk = 8192;
+
+void accept_geometry(int64_t rows, int64_t vocab, int32_t* chunks, int64_t* chunk_elems) {
+  int64_t c = rows > 0 ? (kAcceptTargetBlocks + rows - 1) / rows : 1;
+  c = std::max<int64_t>(1, std::min(c, (vocab + kAcceptMinChunk - 1) / kAcceptMinChunk));
+  int64_t ce = (vocab + c - 1) / c;
+  ce = (ce + 7) & ~int64_t(7);
+  *chunk_elems = std::max<int64_t>(ce, 8);
+  *chunks = int32_t(std::max<int64_t>(1, (vocab + *chunk_elems - 1) / *chunk_elems));
+}
+
+int64_t accept_rows(const ta_plan* plan) { return plan->n_rows + plan->n_branches; }
+
+}  // namespace
+}  // namespace ta
+
+extern "C" int tree_attn_accept_scratch_bytes(const ta_plan* plan, int64_t vocab, size_t* bytes) {
+  if (!plan || !bytes) return fail(TA_ERR_INVALID_ARG, "accept_scratch_bytes: NULL argument");
+  if (plan->kind != TA_PLAN_VERIFY) return fail(TA_ERR_STATE, "accept_scratch_bytes: needs a verify plan");
+  if (vocab < 1 || vocab > INT32_MAX) return fail(TA_ERR_INVALID_ARG, "accept_scratch_bytes: vocab must be in [1, 2^31)");
+  int32_t chunks;
+  int64_t ce;
+  const int64_t rows = accept_rows(plan);
+  accept_geometry(rows, vocab, &chunks, &ce);
+  *bytes = size_t(2 * align256(rows * chunks * 4));
+  return TA_OK;
+}
+
+extern "C" int tree_attn_accept(const ta_plan* plan, int32_t dtype, const void* logits, int64_t vocab, int64_t ld,
+                                const int32_t* tokens, double tau, int32_t mode, int32_t* path, int32_t* n_path,
+                                int32_t* next_token, void* scratch, size_t scratch_bytes, void* stream) {
+  int rc = check_plan(plan, TA_PLAN_VERIFY, "accept");
+  if (rc) return rc;
+  if (dtype != TA_DTYPE_BF16 && dtype != TA_DTYPE_F32)
+    return fail(TA_ERR_UNSUPPORTED, "accept: dtype must be TA_DTYPE_BF16 or TA_DTYPE_F32");
+  if (mode != TA_ACCEPT_TAU && mode != TA_ACCEPT_EXACT) return fail(TA_ERR_INVALID_ARG, "accept: unknown mode");
+  if (mode == TA_ACCEPT_TAU && !(tau > 0.0 && std::isfinite(tau)))
+    return fail(TA_ERR_INVALID_ARG, "accept: tau must be positive and finite");
+  if (vocab < 1 || vocab > INT32_MAX) return fail(TA_ERR_INVALID_ARG, "accept: vocab must be in [1, 2^31)");
+  if (ld < vocab) return fail(TA_ERR_INVALID_ARG, "accept: ld must be >= vocab");
+  const int64_t rows = accept_rows(plan);
+  const int64_t nodes = plan->n_rows;
+  const size_t es = dtype == TA_DTYPE_BF16 ? 2 : 4;
+  if (rows > 0 && (!logits || !aligned(logits, es)))
+    return fail(TA_ERR_INVALID_ARG, "accept: logits is NULL or not aligned to its element size");
+  if (nodes > 0 && (!tokens || !path)) return fail(TA_ERR_INVALID_ARG, "accept: tokens or path is NULL");
+  if (plan->n_branches > 0 && (!n_path || !next_token))
+    return fail(TA_ERR_INVALID_ARG, "accept: n_path or next_token is NULL");
+  int32_t chunks;
+  int64_t ce;
+  accept_geometry(rows, vocab, &chunks, &ce);
+  if (rows * chunks >= (int64_t(1) << 24)) return fail(TA_ERR_CAPACITY, "accept: too many logits rows for one launch");
+  const int64_t half = align256(rows * chunks * 4);
+  if (rows > 0) {
+    if (!scratch) return fail(TA_ERR_WORKSPACE, "accept: scratch is NULL");
+    if (!aligned(scratch, 256)) return fail(TA_ERR_INVALID_ARG, "accept: scratch must be 256-byte aligned");
+    if (int64_t(scratch_bytes) < 2 * half)
+      return fail(TA_ERR_WORKSPACE, "accept: scratch smaller than tree_attn_accept_scratch_bytes");
+  }
+  if ((rc = check_uploaded(plan, "accept"))) return rc;
+  if (plan->n_branches == 0) return TA_OK;
+  AcceptParams p{};
+  p.logits = logits;
+  p.ld = ld;
+  p.vocab = vocab;
+  p.tree_tab = reinterpret_cast<const int32_t*>(static_cast<const unsigned char*>(plan->dev) + plan->layout.trees);
+  p.tokens = tokens;
+  p.n_trees = plan->n_branches;
+  p.exact = mode == TA_ACCEPT_EXACT;
+  p.chunks = chunks;
+  p.chunk_elems = ce;
+  p.part_max = static_cast<float*>(scratch);
+  p.part_idx = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(scratch) + half);
+  p.log_tau = mode == TA_ACCEPT_TAU ? std::log(tau) : 0.0;
+  p.path = path;
+  p.n_path = n_path;
+  p.next_token = next_token;
+  return hip_status(launch_accept(dtype, p, rows, static_cast<hipStream_t>(stream)), "accept launch");
 }

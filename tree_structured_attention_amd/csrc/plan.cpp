@@ -78,6 +78,8 @@ void pack_blob(ta_plan* p) {
   off = align256(off + int64_t(p->merge.size() * sizeof(MergeRow)));
   L.kwork = off;
   off = align256(off + int64_t(p->kwork.size() * sizeof(WorkItem)));
+  L.trees = off;
+  off = align256(off + int64_t(p->tree_tab.size() * 4));
   L.total = std::max<int64_t>(off, 256);
   p->layout = L;
   p->blob.assign(size_t(L.total), 0);
@@ -90,6 +92,7 @@ void pack_blob(ta_plan* p) {
   put(L.mask, p->row_mask.data(), p->row_mask.size() * 8);
   put(L.merge, p->merge.data(), p->merge.size() * sizeof(MergeRow));
   put(L.kwork, p->kwork.data(), p->kwork.size() * sizeof(WorkItem));
+  put(L.trees, p->tree_tab.data(), p->tree_tab.size() * 4);
 }
 
 }  // namespace ta
@@ -427,6 +430,9 @@ extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, co
 
   std::vector<int64_t> node_off(size_t(n_branches) + 1, 0);
   for (int32_t b = 0; b < n_branches; ++b) node_off[b + 1] = node_off[b] + n_nodes[b];
+  pl->tree_tab.reserve(size_t(n_branches) + 1 + size_t(total_nodes));
+  for (int32_t b = 0; b <= n_branches; ++b) pl->tree_tab.push_back(int32_t(node_off[b]));
+  pl->tree_tab.insert(pl->tree_tab.end(), parent, parent + total_nodes);
   for (int32_t b = 0; b < n_branches; ++b) {
     const int32_t p = br_page[b];
     std::vector<uint64_t> bits(static_cast<size_t>(n_nodes[b]));

@@ -60,7 +60,7 @@ static_assert(sizeof(MergeRow) == 32, "merge row layout");
 
 // Offsets (bytes) of the tables inside the device workspace.
 struct DeviceLayout {
-  int64_t work = 0, row_a = 0, row_b = 0, mask = 0, merge = 0, kwork = 0, total = 0;
+  int64_t work = 0, row_a = 0, row_b = 0, mask = 0, merge = 0, kwork = 0, trees = 0, total = 0;
 };
 
 }  // namespace ta
@@ -82,6 +82,7 @@ struct ta_plan {
   std::vector<uint64_t> row_mask;
   std::vector<ta::MergeRow> merge;
   std::vector<ta::WorkItem> kwork;  // prefill: key-major items of the backward
+  std::vector<int32_t> tree_tab;    // verify: node offsets [n_branches + 1], then parents [n_rows]
   ta::DeviceLayout layout;
   std::vector<unsigned char> blob;  // packed image of the device tables
 

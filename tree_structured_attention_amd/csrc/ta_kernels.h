@@ -65,8 +65,27 @@ struct BwdParams {
   int64_t n_rows;
 };
 
+// Greedy acceptance of verified draft trees (tree_attn_accept).
+struct AcceptParams {
+  const void* logits;       // [n_nodes + n_trees rows, ld] bf16 or fp32
+  int64_t ld, vocab;        // row stride and scored entries per row (elements)
+  const int32_t* tree_tab;  // node offsets [n_trees + 1], then parents
+  const int32_t* tokens;    // [n_nodes] drafted token of each node
+  int32_t n_trees;
+  int32_t exact;            // 1: accept only the row's top token
+  int32_t chunks;           // argmax pieces per row
+  int64_t chunk_elems;      // elements per piece (multiple of 8)
+  float* part_max;          // scratch [rows, chunks]
+  int32_t* part_idx;        // scratch [rows, chunks]
+  double log_tau;
+  int32_t* path;            // [n_nodes]: accepted node indices, tree-major
+  int32_t* n_path;          // [n_trees]
+  int32_t* next_token;      // [n_trees]
+};
+
 hipError_t launch_attention(int mode, int dtype, const AttnParams& p, int n_work, int head_dim, hipStream_t st);
 hipError_t launch_merge(int dtype, const MergeParams& p, int head_dim, hipStream_t st);
 hipError_t launch_backward(const BwdParams& p, int n_work, int n_kwork, int head_dim, hipStream_t st);
+hipError_t launch_accept(int dtype, const AcceptParams& p, int64_t n_rows, hipStream_t st);
 
 }  // namespace ta

@@ -294,6 +294,65 @@ def config5(seed: int = 4, with_tensors: bool = True, n_pages: int = 64,
     return w
 
 
+# Vocabulary size of the Qwen-family decoders the pages build on; the pages
+# do not print it, so this is a stand-in for the logits width.
+VOCAB = 151936
+
+
+def draft_tokens(rng, desc: VerifyDesc, vocab: int) -> np.ndarray:
+    """Drafted token of every node, uniform over the vocabulary."""
+    return rng.integers(0, vocab, desc.total_nodes()).astype(np.int32)
+
+
+def accept_logits(seed: int, desc: VerifyDesc, tokens: np.ndarray, vocab: int, ld: int = None,
+                  dtype: torch.dtype = torch.bfloat16, device="cuda", p_plant: float = 0.9) -> torch.Tensor:
+    """Logits rows for the acceptance walk, tree-major: per tree one row for
+    the position after the accepted sequence, then one per node.
+
+    Background scores ~ 1.5 N(0, 1) clipped to [-10, 3]; every row has one
+    top token at 4.0.  In a fraction p_plant of the rows that have children,
+    one child's drafted token is made the top token (70%) or is set to
+    4.0 - gap with gap ~ U(0, 0.6), which straddles log(0.75), so walks of
+    a few accepted nodes occur, as in the acceptance lengths of 2.5 to 4.6
+    tokens per step the HSD notes report.  Columns
+    [vocab, ld) hold 100.0, which the walk must never read."""
+    ld = vocab if ld is None else ld
+    rng = np.random.default_rng(seed)
+    n_trees = desc.n_branches
+    rows = desc.total_nodes() + n_trees
+    g = torch.Generator(device=device).manual_seed(seed)
+    z = torch.randn(rows, ld, generator=g, device=device, dtype=dtype)
+    z.mul_(1.5).clamp_(-10.0, 3.0)
+    top = rng.integers(0, vocab, rows)
+    p_rows, p_tok, p_val = [], [], []
+    off = 0
+    for b in range(n_trees):
+        n = int(desc.n_nodes[b])
+        par = desc.parent[off:off + n]
+        row0 = off + b
+        for r in range(n + 1):
+            kids = np.nonzero(par == r - 1)[0]
+            if len(kids) == 0 or rng.random() >= p_plant:
+                continue
+            c = int(kids[int(rng.integers(len(kids)))])
+            t = int(tokens[off + c])
+            if rng.random() < 0.7:
+                top[row0 + r] = t
+            elif t != top[row0 + r]:
+                p_rows.append(row0 + r)
+                p_tok.append(t)
+                p_val.append(4.0 - rng.uniform(0.0, 0.6))
+        off += n
+    rix = torch.arange(rows, device=device)
+    z[rix, torch.as_tensor(top, device=device)] = 4.0
+    if p_rows:
+        z[torch.as_tensor(p_rows, device=device), torch.as_tensor(p_tok, device=device)] = torch.as_tensor(
+            p_val, device=device, dtype=torch.float32).to(dtype)
+    if ld > vocab:
+        z[:, vocab:] = 100.0
+    return z
+
+
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
