@@ -252,7 +252,10 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   const unsigned char* kb = reinterpret_cast<const unsigned char*>(p.kb) + head_off;
   const unsigned char* vb = reinterpret_cast<const unsigned char*>(p.vb) + head_off;
 
-  TileLoader<T, D, NW> loader;
+  // decode reads each K/V line once (a page's main stream is walked once for
+  // all of its branches and heads), so its copies bypass cache retention;
+  // prefill and verify re-read tiles across row tiles and keep the default
+  TileLoader<T, D, NW, MODE == kDecode ? kCpolStream : 0> loader;
   loader.init(lane, wave, kv_stride);
   // this item's tiles: [tile_lo, tile_hi) of segment A's tiles then B's
   const int it_lo = wi.tile_lo, it_hi = min(wi.tile_hi, n_tiles);

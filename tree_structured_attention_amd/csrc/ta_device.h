@@ -93,8 +93,10 @@ struct TileGeom {
 
 // Global -> LDS copy of one 64-key K/V tile with buffer loads that write LDS
 // directly.  The buffer resource covers only the keys of the segment still
-// to be read, so rows past its end load as zeros (no branches).
-template <typename T, int D, int NW>
+// to be read, so rows past its end load as zeros (no branches).  CPOL is the
+// loads' cache policy (kCpolStream for data no other workgroup reads again).
+constexpr int kCpolStream = 2;  // nt: non-temporal
+template <typename T, int D, int NW, int CPOL = 0>
 struct TileLoader {
   using G = TileGeom<T, D>;
   static constexpr int kRowsPerInst = 64 / G::kChunks;
@@ -122,9 +124,9 @@ struct TileLoader {
 #pragma unroll
     for (int j = 0; j < kInsts; ++j) {
       const int row0 = (j * NW + wave) * kRowsPerInst;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + row0 * G::kRowBytes), 16, voff[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + row0 * G::kRowBytes), 16, voff[j], 0, 0, CPOL);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + G::kTileBytes + row0 * G::kRowBytes), 16,
-                                               voff[j], 0, 0, 0);
+                                               voff[j], 0, 0, CPOL);
     }
   }
 };
