@@ -169,7 +169,8 @@ def accept_case():
     rng = np.random.default_rng(21)
     # host: one tree per branch from 6 region drafts of 100-800 tokens whose
     # last accepted tokens occur in them
-    drafts = [[rng.integers(0, vocab, int(rng.integers(100, 800))).tolist() for _ in range(6)] for _ in range(8)]
+    drafts = [[rng.integers(0, vocab, int(rng.integers(100, 800))).astype(np.int32) for _ in range(6)]
+              for _ in range(8)]
     t0 = time.perf_counter()
     for b in range(desc.n_branches):
         ds = drafts[b % 8]
