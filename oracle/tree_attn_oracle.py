@@ -291,38 +291,50 @@ def prefill_backward_sampled(desc, q, k, v, do, scale: float, rows, keys):
 
 
 def decode(desc, q, k_main, v_main, k_suffix, v_suffix, scale: float, rows=None):
-    """One query token per live branch ([PaDoc] "Inference"; [HPD] shared prefix).
+    """Branch decode over the shared main stream ([PaDoc] "Inference"; [HPD]
+    shared prefix), one or more new tokens per live branch.
 
-    Branch b (page p, region k, s_k earlier tokens) attends to the
-    concatenation main_p[0 : P + L_<=k] ++ suffix_b[0 : s_k + 1], all visible.
-    ``rows`` optionally restricts the computation to some branches (others are
-    returned as zeros).
+    Branch b (page p, region k, s_k earlier tokens, K_b new tokens) owns the
+    suffix rows suffix_b[0 : s_k + K_b]; its query row j (0 <= j < K_b) is
+    suffix token s_k + j and attends to main_p[0 : P + L_<=k] ++
+    suffix_b[0 : s_k + j + 1] (causal among the new tokens).  Region k = 0 is
+    the page's layout stream, which sees the whole main stream.  Rows are
+    branch-major.  ``rows`` optionally restricts the computation to some rows
+    (others are returned as zeros).
     """
     q = _f64(q)
-    nb, hq, d = q.shape
+    nr, hq, d = q.shape
     main_off = np.zeros(desc.n_pages + 1, dtype=np.int64)
     reg_off = np.zeros(desc.n_pages + 1, dtype=np.int64)
     for p in range(desc.n_pages):
         n = int(desc.n_regions[p])
         reg_off[p + 1] = reg_off[p] + n
         main_off[p + 1] = main_off[p] + int(desc.prefix_len[p]) + int(desc.layout_len[reg_off[p]:reg_off[p + 1]].sum())
-    suf_off = np.concatenate([[0], np.cumsum(desc.suffix_len.astype(np.int64) + 1)])
-    o = np.zeros((nb, hq, d))
-    lse = np.zeros((hq, nb))
-    todo = range(nb) if rows is None else rows
-    for b in todo:
+    kq = desc.queries()
+    suf_off = np.concatenate([[0], np.cumsum(desc.suffix_len.astype(np.int64) + kq)])
+    row_off = np.concatenate([[0], np.cumsum(kq)])
+    o = np.zeros((nr, hq, d))
+    lse = np.zeros((hq, nr))
+    todo = set(range(nr)) if rows is None else set(int(r) for r in rows)
+    for b in range(desc.n_branches):
         p = int(desc.br_page[b])
         kreg = int(desc.br_region[b])
-        lay = desc.layout_len[reg_off[p]:reg_off[p] + kreg]
+        n_reg = kreg if kreg > 0 else int(desc.n_regions[p])  # layout stream: all of B
+        lay = desc.layout_len[reg_off[p]:reg_off[p] + n_reg]
         visible_main = int(desc.prefix_len[p]) + int(lay.sum())
         m0 = int(main_off[p])
-        s0, s1 = int(suf_off[b]), int(suf_off[b + 1])
-        kk = np.concatenate([_f64(k_main[m0:m0 + visible_main]), _f64(k_suffix[s0:s1])])
-        vv = np.concatenate([_f64(v_main[m0:m0 + visible_main]), _f64(v_suffix[s0:s1])])
-        mask = np.ones((1, kk.shape[0]), dtype=bool)
-        ob, lb = masked_attention(q[b:b + 1], kk, vv, mask, scale)
-        o[b] = ob[0]
-        lse[:, b] = lb[:, 0]
+        s0 = int(suf_off[b])
+        s = int(desc.suffix_len[b])
+        for j in range(int(kq[b])):
+            r = int(row_off[b]) + j
+            if r not in todo:
+                continue
+            kk = np.concatenate([_f64(k_main[m0:m0 + visible_main]), _f64(k_suffix[s0:s0 + s + j + 1])])
+            vv = np.concatenate([_f64(v_main[m0:m0 + visible_main]), _f64(v_suffix[s0:s0 + s + j + 1])])
+            mask = np.ones((1, kk.shape[0]), dtype=bool)
+            ob, lb = masked_attention(q[r:r + 1], kk, vv, mask, scale)
+            o[r] = ob[0]
+            lse[:, r] = lb[:, 0]
     return o, lse
 
 
@@ -425,8 +437,9 @@ def plan_prefill(desc):
 
 
 def plan_decode(desc):
-    """Per live branch: main_start, main_len (= P + L_<=k), suffix_start,
-    suffix_len (= s_k + 1), position (= P + L_<=k + s_k)."""
+    """Per query row (branch-major): main_start, main_len (= P + L_<=k, the
+    whole main stream for a layout row), suffix_start, visible suffix length
+    (= s_k + j + 1 for new token j), position (= main_len + s_k + j)."""
     rows = []
     main_off = 0
     reg_off = 0
@@ -438,14 +451,18 @@ def plan_decode(desc):
         main_off += int(desc.prefix_len[p]) + int(desc.layout_len[reg_off:reg_off + n].sum())
         reg_off += n
     suf = 0
+    kq = desc.queries()
     for b in range(desc.n_branches):
         p = int(desc.br_page[b])
         k = int(desc.br_region[b])
+        if k == 0:
+            k = int(desc.n_regions[p])
         lay = int(desc.layout_len[regs[p]:regs[p] + k].sum())
         mlen = int(desc.prefix_len[p]) + lay
         s = int(desc.suffix_len[b])
-        rows.append((starts[p], mlen, suf, s + 1, mlen + s))
-        suf += s + 1
+        for j in range(int(kq[b])):
+            rows.append((starts[p], mlen, suf, s + j + 1, mlen + s + j))
+        suf += s + int(kq[b])
     return {"rows": np.array(rows, np.int64).reshape(-1, 5)}
 
 

@@ -385,6 +385,46 @@ def test_decode_equals_prefill_row():
     assert plan["rows"][:, 4].tolist() == oracle.plan_prefill(one_page(P, L, C))["position"][rows].tolist()
 
 
+def test_multi_token_decode_equals_prefill_rows():
+    """K new tokens per branch (a P-MTP window, or a branch's first tokens
+    prefilled over the cached prefix) served over [shared main | own suffix]
+    equal the packed prefill rows of the same tokens; a layout-stream row
+    (region 0) over a page whose last layout region is still being written
+    equals the prefill rows of that region (PaDoc summary, "Inference": the
+    layout stream and the content streams are separate requests over the
+    shared prefix)."""
+    rng = np.random.default_rng(19)
+    P, L = 5, [2, 3, 4]
+    C = [6, 1, 5]
+    s = [2, 0, 1]                       # tokens already in each branch
+    K = [C[i] - s[i] for i in range(3)]  # the rest of each branch is new
+    T = P + sum(L) + sum(C)
+    M = P + sum(L)
+    q, k, v = rand(rng, T, 4, 8), rand(rng, T, 2, 8), rand(rng, T, 2, 8)
+    o_pf, l_pf = oracle.prefill(one_page(P, L, C), q, k, v, 0.35)
+    pos_pf = oracle.plan_prefill(one_page(P, L, C))["position"]
+    # content branches: decode rows are prefill rows [start_k + s_k, end_k)
+    ddesc = synth.DecodeDesc(np.array([P], np.int32), np.array([3], np.int32), np.array(L, np.int32),
+                             np.zeros(3, np.int32), np.array([1, 2, 3], np.int32), np.array(s, np.int32),
+                             np.array(K, np.int32))
+    rows = [M + sum(C[:i]) + s[i] + j for i in range(3) for j in range(K[i])]
+    o_dc, l_dc = oracle.decode(ddesc, q[rows], k[:M], v[:M], k[M:], v[M:], 0.35)
+    assert np.max(np.abs(o_dc - o_pf[rows])) < 1e-12
+    assert np.max(np.abs(l_dc - l_pf[:, rows])) < 1e-12
+    assert oracle.plan_decode(ddesc)["rows"][:, 4].tolist() == pos_pf[rows].tolist()
+    # layout stream: main = X, B_1, B_2; B_3 is its private suffix, 1 token
+    # already written and 3 new ones
+    M2 = P + L[0] + L[1]
+    ldesc = synth.DecodeDesc(np.array([P], np.int32), np.array([2], np.int32), np.array(L[:2], np.int32),
+                             np.zeros(1, np.int32), np.zeros(1, np.int32), np.array([1], np.int32),
+                             np.array([3], np.int32))
+    rows = [M2 + 1 + j for j in range(3)]
+    o_ly, l_ly = oracle.decode(ldesc, q[rows], k[:M2], v[:M2], k[M2:M], v[M2:M], 0.35)
+    assert np.max(np.abs(o_ly - o_pf[rows])) < 1e-12
+    assert np.max(np.abs(l_ly - l_pf[:, rows])) < 1e-12
+    assert oracle.plan_decode(ldesc)["rows"][:, 4].tolist() == pos_pf[rows].tolist()
+
+
 def test_chain_verify_is_causal():
     """A chain tree (parent = previous node) under the tree ancestor mask is
     causal attention over [context | nodes] (HSD notes, key design 3 (b))."""

@@ -28,6 +28,7 @@ Lognormal content lengths: C = clip(rint(exp(5 + 0.8 z)), 8, 1024).
 from __future__ import annotations
 
 from dataclasses import dataclass, field
+from typing import Optional
 
 import numpy as np
 import torch
@@ -67,13 +68,25 @@ class PrefillDesc:
 
 @dataclass
 class DecodeDesc:
-    """Pages' main streams [X | B_1..B_N] plus live branches (page, region k, s_k)."""
+    """Pages' main streams [X | B_1..B_N] plus live rows (page, region k, s_k):
+    content branches (k = 1..N) and layout-stream rows (k = 0, seeing the whole
+    main stream).  Each holds s_k earlier private tokens and n_query new ones
+    (1 unless given), the last n_query of its suffix."""
     prefix_len: np.ndarray   # [n_pages]
     n_regions: np.ndarray    # [n_pages]
     layout_len: np.ndarray   # [sum N]
     br_page: np.ndarray      # [n_branches], non-decreasing
-    br_region: np.ndarray    # [n_branches], 1..N of its page
+    br_region: np.ndarray    # [n_branches], 0 (layout stream) or 1..N of its page
     suffix_len: np.ndarray   # [n_branches], s_k = tokens already in the branch
+    n_query: Optional[np.ndarray] = None  # [n_branches] new tokens (query rows) per branch, >= 1
+
+    def queries(self) -> np.ndarray:
+        if self.n_query is None:
+            return np.ones(self.n_branches, dtype=np.int64)
+        return self.n_query.astype(np.int64)
+
+    def n_rows(self) -> int:
+        return int(self.queries().sum())
 
     @property
     def n_pages(self) -> int:
@@ -93,8 +106,8 @@ class DecodeDesc:
         return out
 
     def suffix_tokens(self) -> int:
-        # every branch stores s_k previous tokens plus the current one
-        return int((self.suffix_len.astype(np.int64) + 1).sum())
+        # every branch stores s_k previous tokens plus its new ones
+        return int((self.suffix_len.astype(np.int64) + self.queries()).sum())
 
 
 @dataclass
@@ -221,7 +234,7 @@ def decode_tensors(rng, desc: DecodeDesc, hq, hkv, d, dtype):
     m = int(desc.main_tokens().sum())
     s = desc.suffix_tokens()
     return {
-        "q": _normal(rng, (desc.n_branches, hq, d), dtype),
+        "q": _normal(rng, (desc.n_rows(), hq, d), dtype),
         "k_main": _normal(rng, (m, hkv, d), dtype),
         "v_main": _normal(rng, (m, hkv, d), dtype),
         "k_suffix": _normal(rng, (s, hkv, d), dtype),
