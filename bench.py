@@ -8,9 +8,11 @@ inputs:
            lognormal content (8,772 tokens), 16q/8kv heads, d = 128, bf16
   decode   16 pages x 24 live branches, P = 4809, s_k ~ U{0..1024}
   verify   64 pages x 8 draft trees of 32 nodes, contexts ~ U{4096..16384}
-The prefill backward (dq, dk, dv of the same page) and the greedy acceptance
-walk over the verify trees (bf16 logits, 151,936-entry vocabulary) are timed
-in the same loop and reported under entries, outside the step.
+The prefill backward (dq, dk, dv of the same page), the greedy acceptance
+walk over the verify trees (bf16 logits, 151,936-entry vocabulary) and a
+multi-token decode (8-token windows for the decode pages' 24 branches plus
+one layout-stream row per page) are timed in the same loop and reported
+under entries, outside the step.
 Each entry point is bracketed by HIP events on the stream it is launched on
 (torch's current stream).  The single JSON line on stdout reports prefill
 packed tokens/s as `value`, with decode and verify beside it, a roofline per
@@ -73,8 +75,8 @@ def prefill_case():
                 flops=flops, bytes=None, bound="mfma", plan_us=plan_us, kernel="attn_kernel<bf16,128,2,prefill> (+ merge_kernel for split tiles)")
 
 
-def decode_case():
-    w = synth.config4()
+def decode_case(w=None, name="decode"):
+    w = w or synth.config4()
     t0 = time.perf_counter()
     plan = ta.plan_for(w.desc)
     plan_us = (time.perf_counter() - t0) * 1e6
@@ -84,26 +86,30 @@ def decode_case():
     lse = torch.empty((w.hq, t["q"].shape[0]), dtype=torch.float32, device="cuda")
     scratch = scratch_for(plan, w)
     info = plan.info
-    rows = plan.export("decode_rows")  # main_start, main_len, suffix_start, suffix_len, position
+    rows = plan.export("decode_rows")  # main_start, main_len, suffix_start, visible suffix, position
 
     def run():
         ta.decode(plan, t["q"], t["k_main"], t["v_main"], t["k_suffix"], t["v_suffix"], scale=w.scale,
                   out=o, lse=lse, scratch=scratch)
 
-    # distinct keys any branch reads: per page the longest visible main prefix, plus every suffix
+    # distinct keys any row reads: per page the longest visible main prefix, plus every suffix token
     main_keys = 0
-    for p in range(w.desc.n_pages):
-        sel = w.desc.br_page == p
-        if sel.any():
-            main_keys += int(rows[sel, 1].max())
-    suffix_keys = int(rows[:, 3].sum())
+    for start in np.unique(rows[:, 0]):
+        main_keys += int(rows[rows[:, 0] == start, 1].max())
+    suffix_keys = w.desc.suffix_tokens()
     e = elt(w.dtype)
     kv_bytes = (main_keys + suffix_keys) * w.hkv * w.head_dim * 2 * e
     qo_bytes = info["n_rows"] * w.hq * w.head_dim * 2 * e + info["n_rows"] * w.hq * 4
     flops = 4.0 * w.head_dim * w.hq * info["visible_pairs"]
-    return dict(name="decode", w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="query tokens",
-                flops=flops, bytes=kv_bytes + qo_bytes, bound="hbm", plan_us=plan_us,
+    return dict(name=name, w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="query tokens",
+                flops=flops, bytes=kv_bytes + qo_bytes, bound="hbm", plan_us=plan_us, in_step=name == "decode",
                 kernel="attn_kernel<bf16,128,2,decode> + merge_kernel")
+
+
+def decode_multi_case():
+    """Drafted windows of 8 new tokens for every live row of the decode pages,
+    plus one layout-stream row per page: timed beside the step."""
+    return decode_case(synth.decode_multi(), "decode_multi")
 
 
 def verify_case():
@@ -252,7 +258,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward", "accept"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward", "accept", "decode_multi"],
+                    default=None,
                     help="time one entry point only (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB three times "
@@ -277,7 +284,7 @@ def main():
     log("[bench] generating inputs")
     cases = []
     for name, fn in (("prefill", prefill_case), ("decode", decode_case), ("verify", verify_case),
-                     ("backward", backward_case), ("accept", accept_case)):
+                     ("backward", backward_case), ("accept", accept_case), ("decode_multi", decode_multi_case)):
         if args.only is None or args.only == name:
             cases.append(fn())
             log(f"[bench] {name}: {cases[-1]['w'].name} ready")
@@ -357,6 +364,8 @@ def main():
         out["backward_mfma_frac"] = per_case["backward"]["roofline"]["frac"]
     if "accept" in per_case:
         out["accept_hbm_frac"] = per_case["accept"]["roofline"]["frac"]
+    if "decode_multi" in per_case:
+        out["decode_multi_hbm_frac"] = per_case["decode_multi"]["roofline"]["frac"]
     if not args.no_cpu_baseline and args.only is None:
         log("[bench] timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)

@@ -68,7 +68,7 @@ extern "C" {
 #define TA_FIELD_BRANCH_START 3 /* prefill: [rows] visible branch keys are [branch_start, row]; row+1 for main tokens */
 #define TA_FIELD_PAGES 4        /* prefill: [pages][5] base, M = P + sum L, T_page, D, D_seq */
 #define TA_FIELD_BRANCHES 5     /* prefill: [branches][3] main_bound (abs), branch_start (abs), length */
-#define TA_FIELD_DECODE_ROWS 6  /* decode:  [branches][5] main_start, main_len, suffix_start, suffix_len, position */
+#define TA_FIELD_DECODE_ROWS 6  /* decode:  [rows][5] main_start, main_len, suffix_start, visible suffix length, position */
 #define TA_FIELD_VERIFY_MASK 7  /* verify:  [nodes] ancestor bitmask (bit j: node j of the same branch is an ancestor or itself) */
 #define TA_FIELD_VERIFY_ROWS 8  /* verify:  [nodes][4] ctx_start, ctx_len, tree_base (abs node 0 of the branch), position */
 #define TA_FIELD_BWD_WORK 10    /* prefill: [items][10] key-major backward items: key0, n_keys, a_lo, a_full, a_hi,
@@ -85,7 +85,7 @@ typedef struct ta_plan_info {
   int32_t n_pages;
   int32_t n_branches;       /* prefill: regions; decode: live branches; verify: trees */
   int32_t n_work;           /* work items of the main launch (per KV head) */
-  int64_t n_rows;           /* query rows: packed tokens / live branches / draft nodes */
+  int64_t n_rows;           /* query rows: packed tokens / decode query rows / draft nodes */
   int64_t n_keys_a;         /* tokens the first key buffer must hold (k / k_main / k_ctx) */
   int64_t n_keys_b;         /* tokens the second key buffer must hold (k / k_suffix / k_tree) */
   int64_t workspace_bytes;  /* device workspace needed by tree_attn_plan_upload */
@@ -122,17 +122,41 @@ int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* n_regions,
  * Document Parsing" notes, "KV cache and shared-prefix reuse").
  *   prefix_len, n_regions, layout_len: the pages' main streams as above
  *   br_page[n_branches]     page of each live branch, non-decreasing
- *   br_region[n_branches]   region k in 1..N of that page
+ *   br_region[n_branches]   region k in 1..N of that page, or 0 for the
+ *                           page's layout stream, which sees the whole main
+ *                           stream (the layout tokens of the region it is
+ *                           writing are its suffix)
  *   suffix_len[n_branches]  s_k >= 0 tokens already generated in the branch
  * Branch b sees main_p[0 : P + L_<=k] and its own s_k + 1 suffix tokens (the
  * current token's K/V must already be appended).  k_main holds the pages'
  * main streams concatenated; k_suffix the branches' suffixes concatenated.
+ * Query rows: one per branch, in branch order.
  */
 int tree_attn_plan_decode(const int32_t* prefix_len, const int32_t* n_regions,
                           const int32_t* layout_len, int32_t n_pages,
                           const int32_t* br_page, const int32_t* br_region,
                           const int32_t* suffix_len, int32_t n_branches,
                           ta_plan** out);
+
+/*
+ * Decode plan with several new tokens per branch: a drafted multi-token
+ * window per branch verified in one pass (the P-MTP drafts of "HPD-Parsing"
+ * notes, Algorithm 1), or a new branch's first tokens prefilled over the
+ * cached prefix ("PaDoc" summary, "Inference": only the unreused suffix and
+ * the branch initialisation need prefill).  Arguments as for
+ * tree_attn_plan_decode, plus
+ *   n_query[n_branches]     K_b >= 1 new tokens of branch b, the last K_b of
+ *                           its s_k + K_b suffix tokens (K/V appended)
+ * Query row j of branch b (rows branch-major, sum K_b in all) is suffix token
+ * s_k + j and sees main_p[0 : P + L_<=k] plus suffix tokens [0, s_k + j]:
+ * causal among the new tokens.  With every K_b = 1 this is
+ * tree_attn_plan_decode.  TA_FIELD_DECODE_ROWS then has one entry per row.
+ */
+int tree_attn_plan_decode_multi(const int32_t* prefix_len, const int32_t* n_regions,
+                                const int32_t* layout_len, int32_t n_pages,
+                                const int32_t* br_page, const int32_t* br_region,
+                                const int32_t* suffix_len, const int32_t* n_query,
+                                int32_t n_branches, ta_plan** out);
 
 /*
  * Verify plan: per-branch draft prefix trees under the tree ancestor mask
@@ -223,8 +247,8 @@ int tree_attn_prefill_backward(const ta_plan* plan, int32_t dtype, int32_t hq, i
 /* Cascade branch decode over a decode plan: pass 1 streams each page's main
  * KV once for all of its branches and query heads and each branch's suffix,
  * writing fp32 partials (m, l, acc) into `scratch`; pass 2 merges them by
- * log-sum-exp in a fixed order.  q, o: [n_branches, Hq, d];
- * k_main/v_main: [sum M_p, Hkv, d]; k_suffix/v_suffix: [sum (s_k+1), Hkv, d];
+ * log-sum-exp in a fixed order.  q, o: [query rows, Hq, d];
+ * k_main/v_main: [sum M_p, Hkv, d]; k_suffix/v_suffix: [sum (s_k+K_b), Hkv, d];
  * scratch: >= tree_attn_scratch_bytes, 256-byte aligned. */
 int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
                      int32_t head_dim, float scale, const void* q, const void* k_main,

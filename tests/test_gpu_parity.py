@@ -197,24 +197,26 @@ def gpu_decode(w, plan=None):
 
 
 def decode_workload(P, N, L, branches, hq=16, hkv=8, d=128, dtype=torch.bfloat16, seed=0):
-    """branches: list of (page, region, s)."""
+    """branches: list of (page, region, s) or (page, region, s, new tokens)."""
     rng = np.random.default_rng(seed)
+    multi = any(len(b) > 3 for b in branches)
     desc = synth.DecodeDesc(np.array(P, np.int32), np.array(N, np.int32), np.array(L, np.int32),
                             np.array([b[0] for b in branches], np.int32),
                             np.array([b[1] for b in branches], np.int32),
-                            np.array([b[2] for b in branches], np.int32))
+                            np.array([b[2] for b in branches], np.int32),
+                            np.array([b[3] if len(b) > 3 else 1 for b in branches], np.int32) if multi else None)
     w = synth.Workload("dec", "decode", desc, hq, hkv, d, dtype, seed=seed)
     w.tensors = synth.decode_tensors(rng, desc, hq, hkv, d, dtype)
     return w
 
 
 def check_decode(w, rows=None, tag=""):
-    say(f"[decode] {tag}: branches={w.desc.n_branches} hq={w.hq} d={w.head_dim} {w.dtype}")
+    say(f"[decode] {tag}: branches={w.desc.n_branches} rows={w.desc.n_rows()} hq={w.hq} d={w.head_dim} {w.dtype}")
     o, lse = gpu_decode(w)
     t = w.tensors
     ro, rl = oracle.decode(w.desc, t["q"], t["k_main"], t["v_main"], t["k_suffix"], t["v_suffix"], w.scale,
                            rows=rows)
-    rows = np.arange(w.desc.n_branches) if rows is None else np.array(rows)
+    rows = np.arange(w.desc.n_rows()) if rows is None else np.array(rows)
     e = close(o[rows], ro[rows], TOL[w.dtype], f"{tag} o")
     close(lse[:, rows], rl[:, rows], LSE_TOL[w.dtype], f"{tag} lse")
     say(f"    max_abs o={e:.3g}")
@@ -237,6 +239,64 @@ def test_decode_config4_full_size_sampled():
     rng = np.random.default_rng(3)
     rows = sorted(set(rng.choice(w.desc.n_branches, 40, replace=False).tolist()) | {0, 23, 383})
     check_decode(w, rows=rows, tag="config4 16 pages x 24 branches")
+
+
+@pytest.mark.parametrize("heads,dtype", [((16, 8, 128), torch.bfloat16), ((4, 4, 64), torch.bfloat16),
+                                         ((8, 2, 32), torch.bfloat16), ((4, 2, 128), torch.float32)])
+def test_decode_multi_small(heads, dtype):
+    hq, hkv, d = heads
+    # several new tokens per branch (1, 3, 8, 64, 65, 130), layout-stream
+    # rows (region 0), suffixes over one chunk with a window, empty s, a page
+    # with no regions, P = 0
+    w = decode_workload([1500, 0, 7, 40], [3, 2, 1, 0], [5, 0, 1200, 3, 4, 2],
+                        [(0, 0, 5, 8), (0, 1, 0, 3), (0, 3, 2100, 65), (0, 2, 70, 1), (1, 0, 0, 130),
+                         (1, 2, 1, 64), (1, 1, 0, 8), (2, 1, 2047, 2), (3, 0, 3, 5)],
+                        hq=hq, hkv=hkv, d=d, dtype=dtype, seed=d + 1)
+    check_decode(w, tag=f"multi small heads={heads}")
+
+
+def test_decode_multi_full_size_sampled():
+    w = synth.decode_multi()
+    rng = np.random.default_rng(5)
+    n = w.desc.n_rows()
+    rows = sorted(set(rng.choice(n, 60, replace=False).tolist()) | {0, 7, 8, 199, n - 1})
+    check_decode(w, rows=rows, tag="16 pages x 25 rows x 8 tokens")
+
+
+def test_decode_multi_equals_prefill_rows():
+    """A branch's new tokens (a window, or its first tokens prefilled over the
+    cached prefix) and a layout-stream window equal the packed prefill rows
+    of the same tokens (both on the GPU, same K/V values)."""
+    P, L, C = 90, [4, 70, 3], [40, 1, 130]
+    s = [0, 0, 100]
+    K = [C[i] - s[i] for i in range(3)]
+    w = prefill_workload(P, L, C, seed=12)
+    o_pf, l_pf = gpu_prefill(w)
+    M = P + sum(L)
+    t = w.tensors
+    ddesc = synth.DecodeDesc(np.array([P], np.int32), np.array([3], np.int32), np.array(L, np.int32),
+                             np.zeros(3, np.int32), np.array([1, 2, 3], np.int32), np.array(s, np.int32),
+                             np.array(K, np.int32))
+    rows = [M + sum(C[:i]) + s[i] + j for i in range(3) for j in range(K[i])]
+    wd = synth.Workload("d", "decode", ddesc, 16, 8, 128, torch.bfloat16,
+                        {"q": t["q"][rows], "k_main": t["k"][:M], "v_main": t["v"][:M],
+                         "k_suffix": t["k"][M:], "v_suffix": t["v"][M:]})
+    o_dc, l_dc = gpu_decode(wd)
+    close(o_dc, o_pf[rows], (2e-2, 1e-2), "multi decode vs prefill o")
+    close(l_dc, l_pf[:, rows], (2e-3, 1e-3), "multi decode vs prefill lse")
+    # layout stream writing B_3: main = X, B_1, B_2; B_3's first token is
+    # already in its suffix, the other two are new
+    M2 = P + L[0] + L[1]
+    ldesc = synth.DecodeDesc(np.array([P], np.int32), np.array([2], np.int32), np.array(L[:2], np.int32),
+                             np.zeros(1, np.int32), np.zeros(1, np.int32), np.array([1], np.int32),
+                             np.array([2], np.int32))
+    rows = [M2 + 1, M2 + 2]
+    wl = synth.Workload("l", "decode", ldesc, 16, 8, 128, torch.bfloat16,
+                        {"q": t["q"][rows], "k_main": t["k"][:M2], "v_main": t["v"][:M2],
+                         "k_suffix": t["k"][M2:M], "v_suffix": t["v"][M2:M]})
+    o_ly, l_ly = gpu_decode(wl)
+    close(o_ly, o_pf[rows], (2e-2, 1e-2), "layout rows vs prefill o")
+    close(l_ly, l_pf[:, rows], (2e-3, 1e-3), "layout rows vs prefill lse")
 
 
 def test_decode_equals_prefill_row():

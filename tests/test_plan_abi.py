@@ -15,7 +15,7 @@ from tree_structured_attention_amd import synth
 def test_library_exports_every_declared_symbol():
     L = ta.lib()
     declared = ta.header_symbols()
-    assert len(declared) == 19
+    assert len(declared) == 20
     for name in declared:
         assert hasattr(L, name), name
     assert L.tree_attn_version().decode().startswith("tree_attn")
@@ -119,6 +119,72 @@ def test_decode_plan_exact():
         assert info["n_keys_b"] == w.desc.suffix_tokens()
 
 
+def check_decode_items(plan, desc):
+    """Every visible (row, key) pair is covered by exactly one work item: main
+    keys through segment A (key < row_a), suffix keys through segment B
+    (key < row_b); no item reaches a key outside the row's stream."""
+    rows = plan.export("decode_rows")
+    work = plan.export("work")
+    n = rows.shape[0]
+    main_cov = [dict() for _ in range(n)]
+    suf_cov = [dict() for _ in range(n)]
+    for w in work:
+        r0, nr, a_lo, a_full, a_hi, b_lo, b_hi = (int(x) for x in w[:7])
+        for r in range(r0, r0 + nr):
+            ms, ml, ss, sl = (int(x) for x in rows[r, :4])
+            for key in range(a_lo, a_hi):
+                if key < ms + ml:
+                    assert key >= ms
+                    main_cov[r][key] = main_cov[r].get(key, 0) + 1
+                elif key < a_full:
+                    raise AssertionError("a key past a row's bound is marked fully visible")
+            for key in range(b_lo, min(b_hi, ss + sl)):
+                assert key >= ss
+                suf_cov[r][key] = suf_cov[r].get(key, 0) + 1
+    for r in range(n):
+        ms, ml, ss, sl = (int(x) for x in rows[r, :4])
+        assert main_cov[r] == {k: 1 for k in range(ms, ms + ml)}, r
+        assert suf_cov[r] == {k: 1 for k in range(ss, ss + sl)}, r
+
+
+def test_decode_multi_plan_exact_and_covering():
+    w = synth.decode_multi(with_tensors=False, n_pages=2)
+    descs = [w.desc]
+    rng = np.random.default_rng(4)
+    for trial in range(6):
+        n_pages = int(rng.integers(1, 4))
+        N = rng.integers(0, 4, n_pages)
+        L = rng.integers(0, 5, int(N.sum()))
+        bp, br, s, kq = [], [], [], []
+        for p in range(n_pages):
+            for _ in range(int(rng.integers(0, 5))):
+                bp.append(p)
+                br.append(int(rng.integers(0, int(N[p]) + 1)))
+                s.append(int(rng.integers(0, 3000 if trial % 2 else 40)))
+                kq.append(int(rng.integers(1, 150 if trial == 3 else 10)))
+        descs.append(synth.DecodeDesc(rng.integers(0, 1500, n_pages).astype(np.int32), N.astype(np.int32),
+                                      L.astype(np.int32), np.array(bp, np.int32), np.array(br, np.int32),
+                                      np.array(s, np.int32), np.array(kq, np.int32)))
+    for desc in descs:
+        plan = ta.plan_for(desc)
+        ref = oracle.plan_decode(desc)
+        assert np.array_equal(plan.export("decode_rows"), ref["rows"])
+        info = plan.info
+        assert info["n_rows"] == desc.n_rows()
+        assert info["n_keys_b"] == desc.suffix_tokens()
+        assert info["visible_pairs"] == int((ref["rows"][:, 1] + ref["rows"][:, 3]).sum())
+        if desc is not descs[0]:
+            check_decode_items(plan, desc)
+    # a single-token multi plan is the plain decode plan
+    w4 = synth.config4(with_tensors=False, n_pages=2)
+    d = w4.desc
+    a = ta.plan_decode(d.prefix_len, d.n_regions, d.layout_len, d.br_page, d.br_region, d.suffix_len)
+    b = ta.plan_decode(d.prefix_len, d.n_regions, d.layout_len, d.br_page, d.br_region, d.suffix_len,
+                       np.ones(d.n_branches, np.int32))
+    for f in ("decode_rows", "work"):
+        assert np.array_equal(a.export(f), b.export(f))
+
+
 def test_verify_plan_exact():
     for w in (synth.config5(with_tensors=False), synth.config5(with_tensors=False, n_pages=3, seed=5)):
         plan = ta.plan_for(w.desc)
@@ -158,6 +224,9 @@ def test_plan_errors():
     expect(ta.TA_ERR_INVALID_ARG, ta.plan_decode, [4, 4], [1, 1], [1, 1], [1, 0], [1, 1], [0, 0])
     expect(ta.TA_ERR_INVALID_ARG, ta.plan_decode, [4], [1], [1], [0], [1], [-1])
     expect(ta.TA_ERR_INVALID_ARG, ta.plan_decode, [4], [1], [1], [1], [1], [0])
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_decode, [4], [1], [1], [0], [-1], [0])
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_decode, [4], [1], [1], [0], [1], [0], [0])
+    expect(ta.TA_ERR_INVALID_ARG, ta.plan_decode, [4], [1], [1], [0, 0], [1, 0], [0, 0], [2, -1])
     # verify: parent not earlier, too many nodes, bad page
     expect(ta.TA_ERR_INVALID_ARG, ta.plan_verify, [5], [0], [3], [-1, 2, 0])
     expect(ta.TA_ERR_INVALID_ARG, ta.plan_verify, [5], [0], [2], [-1, 1])

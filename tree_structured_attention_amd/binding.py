@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
         sig = {
             "tree_attn_plan_prefill": ([_I32P, _I32P, _I32P, _I32P, i32, pp], ctypes.c_int),
             "tree_attn_plan_decode": ([_I32P, _I32P, _I32P, i32, _I32P, _I32P, _I32P, i32, pp], ctypes.c_int),
+            "tree_attn_plan_decode_multi": ([_I32P, _I32P, _I32P, i32, _I32P, _I32P, _I32P, _I32P, i32, pp],
+                                            ctypes.c_int),
             "tree_attn_plan_verify": ([_I32P, i32, _I32P, _I32P, _I32P, i32, pp], ctypes.c_int),
             "tree_attn_plan_info": ([_P, ctypes.POINTER(PlanInfo)], ctypes.c_int),
             "tree_attn_plan_export": ([_P, i32, ctypes.POINTER(i64), i64, ctypes.POINTER(i64)], ctypes.c_int),
@@ -198,12 +200,21 @@ def plan_prefill(prefix_len, n_regions, layout_len, content_len) -> Plan:
     return Plan(out.value, TA_PLAN_PREFILL)
 
 
-def plan_decode(prefix_len, n_regions, layout_len, br_page, br_region, suffix_len) -> Plan:
+def plan_decode(prefix_len, n_regions, layout_len, br_page, br_region, suffix_len, n_query=None) -> Plan:
+    """Decode plan; n_query (new tokens per branch) selects the multi-token
+    form.  br_region 0 is a page's layout stream."""
     P, N, L = _i32(prefix_len), _i32(n_regions), _i32(layout_len)
     bp, br, s = _i32(br_page), _i32(br_region), _i32(suffix_len)
     out = ctypes.c_void_p()
-    _check(lib().tree_attn_plan_decode(_ptr(P), _ptr(N), _ptr(L), int(P.size), _ptr(bp), _ptr(br), _ptr(s),
-                                       int(bp.size), ctypes.byref(out)))
+    if n_query is None:
+        _check(lib().tree_attn_plan_decode(_ptr(P), _ptr(N), _ptr(L), int(P.size), _ptr(bp), _ptr(br), _ptr(s),
+                                           int(bp.size), ctypes.byref(out)))
+    else:
+        kq = _i32(n_query)
+        if kq.size != bp.size:
+            raise TreeAttnError(TA_ERR_INVALID_ARG, "n_query needs one entry per branch")
+        _check(lib().tree_attn_plan_decode_multi(_ptr(P), _ptr(N), _ptr(L), int(P.size), _ptr(bp), _ptr(br),
+                                                 _ptr(s), _ptr(kq), int(bp.size), ctypes.byref(out)))
     return Plan(out.value, TA_PLAN_DECODE)
 
 
@@ -222,7 +233,7 @@ def plan_for(desc) -> Plan:
         return plan_prefill(desc.prefix_len, desc.n_regions, desc.layout_len, desc.content_len)
     if name == "DecodeDesc":
         return plan_decode(desc.prefix_len, desc.n_regions, desc.layout_len, desc.br_page, desc.br_region,
-                           desc.suffix_len)
+                           desc.suffix_len, getattr(desc, "n_query", None))
     if name == "VerifyDesc":
         return plan_verify(desc.ctx_len, desc.br_page, desc.n_nodes, desc.parent)
     raise TypeError(f"no plan for {name}")
@@ -330,6 +341,23 @@ def _heads(q: torch.Tensor, k: torch.Tensor):
     return q.shape[1], k.shape[1], q.shape[2]
 
 
+def _rows(plan: Plan, q, seg_a=(), seg_b=()):
+    """Host-side shape checks against the plan: the kernels index rows and
+    keys from the plan's tables, so short tensors would be read out of
+    bounds."""
+    info = plan_info(plan)
+    if q.shape[0] != info["n_rows"]:
+        raise TreeAttnError(TA_ERR_INVALID_ARG, f"q has {q.shape[0]} rows; the plan has {info['n_rows']}")
+    for t in seg_a:
+        if t is not None and t.shape[0] < info["n_keys_a"]:
+            raise TreeAttnError(TA_ERR_INVALID_ARG, f"a key/value tensor has {t.shape[0]} tokens; the plan needs "
+                                                    f"{info['n_keys_a']}")
+    for t in seg_b:
+        if t is not None and t.shape[0] < info["n_keys_b"]:
+            raise TreeAttnError(TA_ERR_INVALID_ARG, f"a key/value tensor has {t.shape[0]} tokens; the plan needs "
+                                                    f"{info['n_keys_b']}")
+
+
 def _outputs(q, want_lse, out=None, lse=None):
     if out is None:
         out = torch.empty_like(q)
@@ -345,6 +373,7 @@ def _scale(scale, d):
 def prefill(plan: Plan, q, k, v, scale=None, want_lse=True, out=None, lse=None,
             scratch: Optional[torch.Tensor] = None, stream=None):
     hq, hkv, d = _heads(q, k)
+    _rows(plan, q, (k, v), (k, v))
     o, l = _outputs(q, want_lse, out, lse)
     sp, sn = _scratch(plan, hq, d, q.device, scratch)
     _check(lib().tree_attn_prefill(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
@@ -356,6 +385,7 @@ def prefill(plan: Plan, q, k, v, scale=None, want_lse=True, out=None, lse=None,
 def decode(plan: Plan, q, k_main, v_main, k_suffix, v_suffix, scale=None, want_lse=True, out=None, lse=None,
            scratch: Optional[torch.Tensor] = None, stream=None):
     hq, hkv, d = _heads(q, k_main)
+    _rows(plan, q, (k_main, v_main), (k_suffix, v_suffix))
     o, l = _outputs(q, want_lse, out, lse)
     sp, sn = _scratch(plan, hq, d, q.device, scratch)
     _check(lib().tree_attn_decode(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
@@ -367,6 +397,7 @@ def decode(plan: Plan, q, k_main, v_main, k_suffix, v_suffix, scale=None, want_l
 def verify(plan: Plan, q, k_ctx, v_ctx, k_tree, v_tree, scale=None, want_lse=True, out=None, lse=None,
            scratch: Optional[torch.Tensor] = None, stream=None):
     hq, hkv, d = _heads(q, k_ctx)
+    _rows(plan, q, (k_ctx, v_ctx), (k_tree, v_tree))
     o, l = _outputs(q, want_lse, out, lse)
     sp, sn = _scratch(plan, hq, d, q.device, scratch)
     _check(lib().tree_attn_verify(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
@@ -386,6 +417,9 @@ def prefill_backward(plan: Plan, q, k, v, o, lse, d_o, scale=None, dq=None, dk=N
     """Gradients (dq, dk, dv) of the packed forward for output gradient d_o;
     o and lse are the forward's outputs for the same q, k, v."""
     hq, hkv, d = _heads(q, k)
+    _rows(plan, q, (k, v, o, d_o, dk, dv), (k, v))
+    if d_o.shape[0] != q.shape[0] or o.shape[0] != q.shape[0] or (dq is not None and dq.shape[0] != q.shape[0]):
+        raise TreeAttnError(TA_ERR_INVALID_ARG, "o, d_o and dq need one row per query row")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv

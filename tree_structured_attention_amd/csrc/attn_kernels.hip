@@ -124,6 +124,8 @@ struct RowState {
           } else {
             if constexpr (MODE == kPrefill) {
               vis = vis & (!row_ok | ((key >= rb) & (key <= row)));
+            } else if constexpr (MODE == kDecode) {
+              vis = vis & (!row_ok | (key < rb));
             } else if constexpr (MODE == kVerify) {
               const unsigned rel = unsigned(key - rb);
               const uint32_t word = rel < 32u ? uint32_t(rmask) : uint32_t(rmask >> 32);
@@ -244,7 +246,9 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   const int n_tiles = n_a + n_b;
   // tiles [0, fa) of segment A and [n_a, n_a + fb) of segment B need no mask
   const int fa = min(n_a, max(0, wi.a_full - wi.a_lo) / kKeyTile);
-  const int fb = (wi.flags & kSegBFull) ? (wi.b_hi - wi.b_lo) / kKeyTile : 0;
+  const int fb = (wi.flags & kSegBFull)  ? (wi.b_hi - wi.b_lo) / kKeyTile
+                 : MODE == kDecode        ? max(0, wi.b_full - wi.b_lo) / kKeyTile
+                                          : 0;
   const int64_t kv_stride = int64_t(p.hkv) * D * Elt<T>::kBytes;
   const int64_t head_off = int64_t(kvh) * D * Elt<T>::kBytes;
   const unsigned char* ka = reinterpret_cast<const unsigned char*>(p.ka) + head_off;
@@ -397,7 +401,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   float mx = -INFINITY;
   for (int c = 0; c < mr.sh_count; ++c)
     mx = fmaxf(mx, p.part_ml[(int64_t(mr.sh_first + c * mr.sh_stride) * p.hq + head) * 2]);
-  for (int c = 0; c < mr.sf_count; ++c) mx = fmaxf(mx, p.part_ml[(int64_t(mr.sf_first + c) * p.hq + head) * 2]);
+  for (int c = 0; c < mr.sf_count; ++c)
+    mx = fmaxf(mx, p.part_ml[((int64_t(mr.sf_first) + int64_t(c) * mr.sf_stride) * p.hq + head) * 2]);
   float acc[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) acc[j] = 0.f;
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int n_parts = mr.sh_count + mr.sf_count;
   for (int c = 0; c < n_parts; ++c) {
     const int64_t slot = c < mr.sh_count ? int64_t(mr.sh_first) + int64_t(c) * mr.sh_stride
-                                         : int64_t(mr.sf_first) + (c - mr.sh_count);
+                                         : int64_t(mr.sf_first) + int64_t(c - mr.sh_count) * mr.sf_stride;
     const int64_t idx = slot * p.hq + head;
     const float m = p.part_ml[idx * 2];
     const float w = (m == -INFINITY) ? 0.f : fast_exp2(m - mx);

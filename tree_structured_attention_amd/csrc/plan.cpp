@@ -52,6 +52,7 @@ WorkItem make_item(int64_t row0, int64_t nrows, int64_t a_lo, int64_t a_full, in
   w.b_hi = int32_t(std::max(b_lo, b_hi));
   w.out = int32_t(out);
   w.flags = flags;
+  w.b_full = w.b_lo;
   w.tile_lo = 0;
   w.tile_hi = int32_t(item_tiles(w));
   return w;
@@ -258,11 +259,12 @@ extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* 
   return TA_OK;
 }
 
-extern "C" int tree_attn_plan_decode(const int32_t* prefix_len, const int32_t* n_regions,
-                                     const int32_t* layout_len, int32_t n_pages,
-                                     const int32_t* br_page, const int32_t* br_region,
-                                     const int32_t* suffix_len, int32_t n_branches,
-                                     ta_plan** out) {
+namespace {
+
+// Decode plan with n_query[b] new tokens per live branch (NULL: one each).
+int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int32_t* layout_len, int32_t n_pages,
+                 const int32_t* br_page, const int32_t* br_region, const int32_t* suffix_len,
+                 const int32_t* n_query, int32_t n_branches, ta_plan** out) {
   if (!out) return fail(TA_ERR_INVALID_ARG, "plan_decode: out is NULL");
   if (n_pages < 0 || n_branches < 0) return fail(TA_ERR_INVALID_ARG, "plan_decode: negative count");
   if (n_pages > 0 && (!prefix_len || !n_regions))
@@ -284,58 +286,70 @@ extern "C" int tree_attn_plan_decode(const int32_t* prefix_len, const int32_t* n
     main_off[p + 1] = main_off[p] + m;
     if (main_off[p + 1] >= kMax32) return fail(TA_ERR_CAPACITY, "plan_decode: main tokens >= 2^31");
   }
-  int64_t suffix_total = 0;
+  auto kq = [&](int32_t b) -> int64_t { return n_query ? n_query[b] : 1; };
+  int64_t suffix_total = 0, rows_total = 0;
   for (int32_t b = 0; b < n_branches; ++b) {
     if (br_page[b] < 0 || br_page[b] >= n_pages) return fail(TA_ERR_INVALID_ARG, "plan_decode: br_page out of range");
     if (b > 0 && br_page[b] < br_page[b - 1])
       return fail(TA_ERR_INVALID_ARG, "plan_decode: branches must be grouped by page (br_page non-decreasing)");
-    if (br_region[b] < 1 || br_region[b] > n_regions[br_page[b]])
-      return fail(TA_ERR_INVALID_ARG, "plan_decode: br_region must be in 1..N of its page");
+    if (br_region[b] < 0 || br_region[b] > n_regions[br_page[b]])
+      return fail(TA_ERR_INVALID_ARG, "plan_decode: br_region must be 0 (layout stream) or 1..N of its page");
     if (suffix_len[b] < 0) return fail(TA_ERR_INVALID_ARG, "plan_decode: negative suffix_len");
-    suffix_total += int64_t(suffix_len[b]) + 1;
+    if (kq(b) < 1) return fail(TA_ERR_INVALID_ARG, "plan_decode: n_query must be >= 1");
+    suffix_total += int64_t(suffix_len[b]) + kq(b);
+    rows_total += kq(b);
     if (suffix_total >= kMax32) return fail(TA_ERR_CAPACITY, "plan_decode: suffix tokens >= 2^31");
+    if (rows_total >= kMax32) return fail(TA_ERR_CAPACITY, "plan_decode: query rows >= 2^31");
   }
 
   auto* pl = new ta_plan();
   pl->kind = TA_PLAN_DECODE;
   pl->n_pages = n_pages;
   pl->n_branches = n_branches;
-  pl->n_rows = n_branches;
+  pl->n_rows = rows_total;
   pl->n_keys_a = main_off[n_pages];
   pl->n_keys_b = suffix_total;
-  pl->row_a.resize(size_t(n_branches));
-  pl->row_b.assign(size_t(n_branches), 0);
-  pl->merge.resize(size_t(n_branches));
+  pl->row_a.resize(size_t(rows_total));
+  pl->row_b.resize(size_t(rows_total));
+  pl->merge.resize(size_t(rows_total));
 
-  std::vector<int64_t> main_len(static_cast<size_t>(n_branches)), suf_start(static_cast<size_t>(n_branches));
+  // per row: main bound (page-relative); per branch: first row, suffix start
+  std::vector<int64_t> main_len(static_cast<size_t>(rows_total));
+  std::vector<int64_t> row_off(static_cast<size_t>(n_branches) + 1, 0), suf_start(static_cast<size_t>(n_branches));
   int64_t s0 = 0;
   for (int32_t b = 0; b < n_branches; ++b) {
     const int32_t p = br_page[b];
+    const int32_t n_reg = br_region[b] > 0 ? br_region[b] : n_regions[p];  // layout stream: all of B
     int64_t m = prefix_len[p];
-    for (int32_t k = 0; k < br_region[b]; ++k) m += layout_len[reg_off[p] + k];
-    main_len[b] = m;
+    for (int32_t k = 0; k < n_reg; ++k) m += layout_len[reg_off[p] + k];
     suf_start[b] = s0;
-    pl->row_a[b] = int32_t(main_off[p] + m);
-    pl->decode_rows5.insert(pl->decode_rows5.end(),
-                            {main_off[p], m, s0, int64_t(suffix_len[b]) + 1, m + suffix_len[b]});
-    pl->visible_pairs += m + suffix_len[b] + 1;
-    s0 += int64_t(suffix_len[b]) + 1;
+    row_off[b + 1] = row_off[b] + kq(b);
+    for (int64_t j = 0; j < kq(b); ++j) {
+      const int64_t r = row_off[b] + j;
+      const int64_t vis_suffix = int64_t(suffix_len[b]) + j + 1;
+      main_len[r] = m;
+      pl->row_a[r] = int32_t(main_off[p] + m);
+      pl->row_b[r] = int32_t(s0 + vis_suffix);
+      pl->decode_rows5.insert(pl->decode_rows5.end(), {main_off[p], m, s0, vis_suffix, m + vis_suffix - 1});
+      pl->visible_pairs += m + vis_suffix;
+    }
+    s0 += int64_t(suffix_len[b]) + kq(b);
   }
 
   // Pass-1 work items.  Partial slots (per query head) are numbered in plan
-  // order: a shared chunk owns one slot per branch of its row group, a
-  // suffix chunk one slot.
+  // order: a shared chunk owns one slot per row of its row group, and so does
+  // a suffix chunk.
   int64_t slot = 0;
   int32_t b = 0;
   while (b < n_branches) {
     const int32_t p = br_page[b];
     int32_t e = b;
     while (e < n_branches && br_page[e] == p) ++e;
-    // row groups of at most one tile of branches
-    for (int32_t g0 = b; g0 < e; g0 += kTileTokens) {
-      const int32_t g1 = std::min(e, g0 + kTileTokens);
+    // row groups of at most one tile of the page's rows
+    for (int64_t g0 = row_off[b]; g0 < row_off[e]; g0 += kTileTokens) {
+      const int64_t g1 = std::min(row_off[e], g0 + kTileTokens);
       int64_t hi = 0, lo_bound = INT64_MAX;
-      for (int32_t i = g0; i < g1; ++i) {
+      for (int64_t i = g0; i < g1; ++i) {
         hi = std::max(hi, main_len[i]);
         lo_bound = std::min(lo_bound, main_len[i]);
       }
@@ -347,26 +361,40 @@ extern "C" int tree_attn_plan_decode(const int32_t* prefix_len, const int32_t* n
                                      0, 0, slot, 0));
         slot += g1 - g0;
       }
-      for (int32_t i = g0; i < g1; ++i) {
+      for (int64_t i = g0; i < g1; ++i) {
         MergeRow& mr = pl->merge[i];
-        mr.row = i;
+        mr.row = int32_t(i);
         mr.sh_first = int32_t(first + (i - g0));
         mr.sh_count = int32_t((main_len[i] + kDecodeChunk - 1) / kDecodeChunk);
-        mr.sh_stride = g1 - g0;
+        mr.sh_stride = int32_t(g1 - g0);
       }
     }
     b = e;
   }
+  // Suffix items: per branch, row groups of at most one tile of its new
+  // tokens; row j of the branch sees suffix keys [start, start + s + j + 1).
   for (int32_t i = 0; i < n_branches; ++i) {
-    const int64_t len = int64_t(suffix_len[i]) + 1;
-    const int64_t chunk = len <= kDecodeSuffixWhole ? len : kDecodeChunk;
-    const int64_t n_chunks = (len + chunk - 1) / chunk;
-    pl->merge[i].sf_first = int32_t(slot);
-    pl->merge[i].sf_count = int32_t(n_chunks);
-    for (int64_t c = 0; c < n_chunks; ++c) {
-      const int64_t c0 = suf_start[i] + c * chunk, c1 = std::min(suf_start[i] + len, c0 + chunk);
-      pl->work.push_back(make_item(i, 1, 0, 0, 0, c0, c1, slot, kSegBFull));
-      slot += 1;
+    const int64_t s = suffix_len[i];
+    for (int64_t j0 = 0; j0 < kq(i); j0 += kTileTokens) {
+      const int64_t j1 = std::min(kq(i), j0 + kTileTokens);
+      const int64_t len = s + j1;             // keys the group's last row sees
+      const int64_t full = suf_start[i] + s + j0 + 1;  // keys every row of the group sees end here
+      const int64_t chunk = len <= kDecodeSuffixWhole ? len : kDecodeChunk;
+      const int64_t n_chunks = (len + chunk - 1) / chunk;
+      const int64_t first = slot;
+      for (int64_t c = 0; c < n_chunks; ++c) {
+        const int64_t c0 = suf_start[i] + c * chunk, c1 = std::min(suf_start[i] + len, c0 + chunk);
+        WorkItem w = make_item(row_off[i] + j0, j1 - j0, 0, 0, 0, c0, c1, slot, c1 <= full ? kSegBFull : 0);
+        w.b_full = int32_t(std::max(c0, std::min(c1, full)));
+        pl->work.push_back(w);
+        slot += j1 - j0;
+      }
+      for (int64_t j = j0; j < j1; ++j) {
+        MergeRow& mr = pl->merge[row_off[i] + j];
+        mr.sf_first = int32_t(first + (j - j0));
+        mr.sf_count = int32_t((s + j + 1 + chunk - 1) / chunk);
+        mr.sf_stride = int32_t(j1 - j0);
+      }
     }
   }
   if (slot >= kMax32) {
@@ -378,6 +406,27 @@ extern "C" int tree_attn_plan_decode(const int32_t* prefix_len, const int32_t* n
   pack_blob(pl);
   *out = pl;
   return TA_OK;
+}
+
+}  // namespace
+
+extern "C" int tree_attn_plan_decode(const int32_t* prefix_len, const int32_t* n_regions,
+                                     const int32_t* layout_len, int32_t n_pages,
+                                     const int32_t* br_page, const int32_t* br_region,
+                                     const int32_t* suffix_len, int32_t n_branches,
+                                     ta_plan** out) {
+  return build_decode(prefix_len, n_regions, layout_len, n_pages, br_page, br_region, suffix_len, nullptr,
+                      n_branches, out);
+}
+
+extern "C" int tree_attn_plan_decode_multi(const int32_t* prefix_len, const int32_t* n_regions,
+                                           const int32_t* layout_len, int32_t n_pages,
+                                           const int32_t* br_page, const int32_t* br_region,
+                                           const int32_t* suffix_len, const int32_t* n_query,
+                                           int32_t n_branches, ta_plan** out) {
+  if (n_branches > 0 && !n_query) return fail(TA_ERR_INVALID_ARG, "plan_decode_multi: NULL n_query");
+  return build_decode(prefix_len, n_regions, layout_len, n_pages, br_page, br_region, suffix_len, n_query,
+                      n_branches, out);
 }
 
 extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page,
@@ -557,6 +606,7 @@ extern "C" int tree_attn_plan_balance(ta_plan* plan, int32_t n_kv_heads, int32_t
       mr.sh_stride = w.nrows;
       mr.sf_first = 0;
       mr.sf_count = 0;
+      mr.sf_stride = 1;
       mr.row = w.row0 + t;
       merge.push_back(mr);
     }

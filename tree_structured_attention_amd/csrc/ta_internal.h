@@ -24,8 +24,10 @@ constexpr int kDecodeSuffixWhole = 2048;
 //   rows  [row0, row0 + nrows)
 //   seg A [a_lo, a_hi): keys [a_lo, a_full) are visible to every row of the
 //         tile; keys in [a_full, a_hi) are tested per row against row_a.
-//   seg B [b_lo, b_hi): always tested per row (prefill: branch-causal;
-//         verify: tree bitmask; decode suffix: visible, flag kSegBFull).
+//   seg B [b_lo, b_hi): tested per row (prefill: branch-causal; verify:
+//         tree bitmask; decode suffix: key < row_b, so keys [b_lo, b_full)
+//         are visible to every row of the tile and flag kSegBFull marks a
+//         segment visible to all of them).
 //   out   first partial slot of the tile (per query head) when the item
 //         writes fp32 partials (decode; split prefill/verify pieces); else -1.
 //   flags bit 0: seg B fully visible.
@@ -34,7 +36,7 @@ constexpr int kDecodeSuffixWhole = 2048;
 //         one item per piece.
 struct WorkItem {
   int32_t row0, nrows, a_lo, a_full, a_hi, b_lo, b_hi, out;
-  int32_t flags, tile_lo, tile_hi, pad0;
+  int32_t flags, tile_lo, tile_hi, b_full;
 };
 static_assert(sizeof(WorkItem) == 48, "work item layout");
 constexpr int32_t kSegBFull = 1;
@@ -50,11 +52,11 @@ constexpr int32_t kSegBFull = 1;
 constexpr int32_t kKeyBranch = 2;
 
 // Merge table, one entry per output row combined from partials: slots are
-// sh_first + c * sh_stride (c < sh_count), then sf_first + c (c < sf_count),
-// merged in that order.  Decode: every branch (main-stream chunks, then its
+// sh_first + c * sh_stride (c < sh_count), then sf_first + c * sf_stride
+// (c < sf_count), merged in that order.  Decode: every branch (main-stream chunks, then its
 // suffix chunks).  Prefill/verify: the rows of split row tiles.
 struct MergeRow {
-  int32_t sh_first, sh_count, sh_stride, sf_first, sf_count, row, pad0, pad1;
+  int32_t sh_first, sh_count, sh_stride, sf_first, sf_count, row, sf_stride, pad0;
 };
 static_assert(sizeof(MergeRow) == 32, "merge row layout");
 

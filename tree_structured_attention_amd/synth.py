@@ -260,6 +260,31 @@ def config4(seed: int = 3, with_tensors: bool = True, n_pages: int = 16) -> Work
     return w
 
 
+def decode_multi(seed: int = 6, with_tensors: bool = True, n_pages: int = 16, window: int = 8) -> Workload:
+    """The decode workload's pages with a drafted window of `window` new tokens
+    per live row: per page one layout-stream row (region 0, 0..11 layout
+    tokens of its current region already written) followed by 24 content
+    branches with s_k ~ U{0..1024}."""
+    rng = np.random.default_rng(seed)
+    s_lay = rng.integers(0, 12, n_pages)
+    s_br = rng.integers(0, 1025, (n_pages, 24))
+    suffix = np.concatenate([[s_lay[p]] + list(s_br[p]) for p in range(n_pages)]).astype(np.int32)
+    desc = DecodeDesc(
+        prefix_len=np.full(n_pages, 4809, dtype=np.int32),
+        n_regions=np.full(n_pages, 24, dtype=np.int32),
+        layout_len=np.full(24 * n_pages, 12, dtype=np.int32),
+        br_page=np.repeat(np.arange(n_pages, dtype=np.int32), 25),
+        br_region=np.tile(np.arange(0, 25, dtype=np.int32), n_pages),
+        suffix_len=suffix,
+        n_query=np.full(25 * n_pages, window, dtype=np.int32),
+    )
+    w = Workload(f"decode_multi_{n_pages}pages_x(1+24)rows_x{window}tokens_P4809", "decode", desc, 16, 8, 128,
+                 torch.bfloat16, seed=seed)
+    if with_tensors:
+        w.tensors = decode_tensors(rng, desc, 16, 8, 128, torch.bfloat16)
+    return w
+
+
 def random_tree_parents(rng, n_nodes: int, max_children: int = 3, max_depth: int = 8) -> np.ndarray:
     """Node 0 is the root (depth 0, hangs off the context); node i picks its
     parent uniformly among earlier nodes with < max_children children and
