@@ -28,3 +28,4 @@ from .draft_oracle import (  # noqa: F401,E402
     tree_accept,
     chain_accept,
 )
+from .kv_pool_oracle import KVPool, PoolError, gather as gather_paged  # noqa: F401,E402
