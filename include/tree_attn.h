@@ -75,6 +75,9 @@ extern "C" {
                                    b_lo, b_hi, b_full, flags (2: branch-area keys), row tiles walked; rows
                                    [a_lo, a_hi) and [b_lo, b_hi) can see the keys, rows from a_full / b_full on
                                    see all of them */
+#define TA_FIELD_PAGED_TILES 11 /* paged: [tiles of A, then tiles of B] cache row of the first token of each
+                                   64-token tile, by virtual position / 64 (A: main streams or contexts; B: decode
+                                   suffixes, absent for verify) */
 #define TA_FIELD_WORK 9         /* any:     [work][10] the launch work list: row0, nrows, a_lo, a_full, a_hi, b_lo, b_hi,
                                            partial slot (-1: direct), tile_lo, tile_hi (diagnostic; order is not contractual) */
 
@@ -176,6 +179,89 @@ int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages,
                           const int32_t* br_page, const int32_t* n_nodes,
                           const int32_t* parent, int32_t n_branches,
                           ta_plan** out);
+
+/*
+ * Paged plans: the same decode (any n_query; NULL = one token per branch) and
+ * verify plans with the long key streams read from a block-paged KV cache
+ * instead of concatenated buffers (zero-copy shared-prefix KV: "HPD-Parsing"
+ * notes, "KV cache and shared-prefix reuse"; "PaDoc" summary, "Inference":
+ * branches reuse the complete KV blocks of the shared prefix).
+ *   block_size        tokens per block, a positive multiple of 64 (a 64-key
+ *                     tile never straddles two blocks)
+ *   n_cache_blocks    blocks in the cache; the cache tensors passed to the
+ *                     launch are [n_cache_blocks * block_size, Hkv, d]
+ *   token t of sequence i lives in cache row
+ *                     blocks[block_off[i] + t / block_size] * block_size
+ *                     + t % block_size; a table needs ceil(len / block_size)
+ *                     entries, each in [0, n_cache_blocks)
+ * Decode: main_blocks/main_block_off[n_pages + 1] map each page's main stream
+ * (length P + sum L), suffix_blocks/suffix_block_off[n_branches + 1] each
+ * branch's suffix (length s_k + K_b).  Branches of a page may share blocks
+ * with its main stream and with each other; a branch's row reads the main
+ * table only below its bound, so blocks written past it do not matter.
+ * Pass the cache as k_main/v_main and as k_suffix/v_suffix (or two caches of
+ * the same geometry).  Verify: ctx_blocks/ctx_block_off[n_pages + 1] map each
+ * page's context; k_tree/v_tree stay contiguous.  Exported positions
+ * (TA_FIELD_DECODE_ROWS, TA_FIELD_VERIFY_ROWS) of paged plans are virtual:
+ * every sequence starts at a multiple of 64.  n_keys_a (and n_keys_b of
+ * paged decode) report the cache rows, n_cache_blocks * block_size.
+ * Errors as for the unpaged plans, plus INVALID_ARG for a bad block size,
+ * short tables or block ids out of range, CAPACITY for caches of 2^31 rows.
+ */
+int tree_attn_plan_decode_paged(const int32_t* prefix_len, const int32_t* n_regions,
+                                const int32_t* layout_len, int32_t n_pages,
+                                const int32_t* br_page, const int32_t* br_region,
+                                const int32_t* suffix_len, const int32_t* n_query,
+                                int32_t n_branches, int32_t block_size, int32_t n_cache_blocks,
+                                const int32_t* main_blocks, const int64_t* main_block_off,
+                                const int32_t* suffix_blocks, const int64_t* suffix_block_off,
+                                ta_plan** out);
+int tree_attn_plan_verify_paged(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page,
+                                const int32_t* n_nodes, const int32_t* parent, int32_t n_branches,
+                                int32_t block_size, int32_t n_cache_blocks, const int32_t* ctx_blocks,
+                                const int64_t* ctx_block_off, ta_plan** out);
+
+/*
+ * Block pool of a paged KV cache, on the host (HPD-Parsing notes,
+ * "KV cache and shared-prefix reuse" and Algorithm 1: a forked branch points
+ * at its parent's KV blocks without copying them; KV is released by
+ * reference count).  The pool decides which cache rows hold which tokens;
+ * the caller owns the device cache and writes K/V at the slots it is given.
+ * Not thread-safe.
+ *   create(n_blocks, block_size)   empty pool; free blocks are handed out
+ *                                  lowest id first
+ *   new_seq                        a root sequence (e.g. a page's main
+ *                                  stream: prefix + layout stream)
+ *   fork(parent, n_tokens)         a branch that views the root's first
+ *                                  n_tokens (its blocks gain a reference)
+ *                                  and owns tokens of its own; forks are
+ *                                  taken from live roots only
+ *   append(seq, n, slots[n])       room for n more own tokens; slots get
+ *                                  their cache rows (block * block_size +
+ *                                  offset).  All or nothing: CAPACITY, and no
+ *                                  change, if the free blocks do not suffice
+ *   release(seq)                   drops the sequence's references; blocks
+ *                                  with none left are free again (a root's
+ *                                  blocks stay while forks view them)
+ *   table(seq, ...)                the view's blocks and token count, and the
+ *                                  own blocks and token count (counts are
+ *                                  written even when a capacity is short:
+ *                                  then WORKSPACE)
+ *   refs(refs[n_blocks], *free)    reference count of every block (refs may
+ *                                  be NULL) and the number of free blocks
+ * Sequence ids count up from 0 and are never reused; INVALID_ARG for an
+ * unknown or released id.
+ */
+typedef struct ta_kv_pool ta_kv_pool;
+int tree_attn_pool_create(int32_t n_blocks, int32_t block_size, ta_kv_pool** out);
+void tree_attn_pool_destroy(ta_kv_pool* pool);
+int tree_attn_pool_new_seq(ta_kv_pool* pool, int32_t* seq);
+int tree_attn_pool_fork(ta_kv_pool* pool, int32_t parent, int32_t n_tokens, int32_t* child);
+int tree_attn_pool_append(ta_kv_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots);
+int tree_attn_pool_release(ta_kv_pool* pool, int32_t seq);
+int tree_attn_pool_table(const ta_kv_pool* pool, int32_t seq, int32_t* view, int32_t view_cap,
+                         int32_t* view_tokens, int32_t* own, int32_t own_cap, int32_t* own_tokens);
+int tree_attn_pool_refs(const ta_kv_pool* pool, int32_t* refs, int32_t cap, int32_t* free_blocks);
 
 int tree_attn_plan_info(const ta_plan* plan, ta_plan_info* out);
 

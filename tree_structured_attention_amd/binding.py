@@ -50,6 +50,7 @@ FIELD = {
     "verify_rows": 8,
     "work": 9,
     "bwd_work": 10,
+    "paged_tiles": 11,
 }
 FIELD_WIDTH = {"pages": 5, "branches": 3, "decode_rows": 5, "verify_rows": 4, "work": 10, "bwd_work": 10}
 
@@ -82,6 +83,7 @@ class PlanInfo(ctypes.Structure):
 _lib = None
 _P = ctypes.c_void_p
 _I32P = ctypes.POINTER(ctypes.c_int32)
+_I64P = ctypes.POINTER(ctypes.c_int64)
 
 
 def lib() -> ctypes.CDLL:
@@ -101,6 +103,18 @@ def lib() -> ctypes.CDLL:
             "tree_attn_plan_decode_multi": ([_I32P, _I32P, _I32P, i32, _I32P, _I32P, _I32P, _I32P, i32, pp],
                                             ctypes.c_int),
             "tree_attn_plan_verify": ([_I32P, i32, _I32P, _I32P, _I32P, i32, pp], ctypes.c_int),
+            "tree_attn_plan_decode_paged": ([_I32P, _I32P, _I32P, i32, _I32P, _I32P, _I32P, _I32P, i32, i32, i32,
+                                             _I32P, _I64P, _I32P, _I64P, pp], ctypes.c_int),
+            "tree_attn_plan_verify_paged": ([_I32P, i32, _I32P, _I32P, _I32P, i32, i32, i32, _I32P, _I64P, pp],
+                                            ctypes.c_int),
+            "tree_attn_pool_create": ([i32, i32, pp], ctypes.c_int),
+            "tree_attn_pool_destroy": ([_P], None),
+            "tree_attn_pool_new_seq": ([_P, _I32P], ctypes.c_int),
+            "tree_attn_pool_fork": ([_P, i32, i32, _I32P], ctypes.c_int),
+            "tree_attn_pool_append": ([_P, i32, i32, _I64P], ctypes.c_int),
+            "tree_attn_pool_release": ([_P, i32], ctypes.c_int),
+            "tree_attn_pool_table": ([_P, i32, _I32P, i32, _I32P, _I32P, i32, _I32P], ctypes.c_int),
+            "tree_attn_pool_refs": ([_P, _I32P, i32, _I32P], ctypes.c_int),
             "tree_attn_plan_info": ([_P, ctypes.POINTER(PlanInfo)], ctypes.c_int),
             "tree_attn_plan_export": ([_P, i32, ctypes.POINTER(i64), i64, ctypes.POINTER(i64)], ctypes.c_int),
             "tree_attn_plan_upload": ([_P, _P, sz, _P], ctypes.c_int),
@@ -505,3 +519,104 @@ def accept(plan: Plan, logits, tokens, tau: float = 0.75, exact: bool = False, v
                                   _dev_ptr(n_path), _dev_ptr(next_token), ctypes.c_void_p(view.data_ptr()),
                                   view.numel(), _stream_handle(stream)))
     return path[:n_nodes], n_path[:n_trees], next_token[:n_trees]
+
+
+# ---------------------------------------------------------------------------
+# paged KV: plans over block tables, and the host block pool
+# ---------------------------------------------------------------------------
+
+def _tables(tables):
+    """List of per-sequence block lists -> (concatenated int32, int64 offsets)."""
+    off = np.zeros(len(tables) + 1, np.int64)
+    for i, tb in enumerate(tables):
+        off[i + 1] = off[i] + len(tb)
+    cat = np.ascontiguousarray(np.concatenate([np.asarray(tb, np.int32) for tb in tables])
+                               if tables and off[-1] else np.zeros(0, np.int32), dtype=np.int32)
+    return cat, off
+
+
+def _p64(a: np.ndarray):
+    return a.ctypes.data_as(_I64P) if a.size else None
+
+
+def plan_decode_paged(prefix_len, n_regions, layout_len, br_page, br_region, suffix_len, n_query,
+                      block_size: int, n_cache_blocks: int, main_tables, suffix_tables) -> Plan:
+    """Decode plan whose main streams and suffixes live in a paged cache:
+    main_tables[p] / suffix_tables[b] are block-id lists."""
+    P, N, L = _i32(prefix_len), _i32(n_regions), _i32(layout_len)
+    bp, br, s = _i32(br_page), _i32(br_region), _i32(suffix_len)
+    kq = None if n_query is None else _i32(n_query)
+    mb, mo = _tables(main_tables)
+    sb, so = _tables(suffix_tables)
+    out = ctypes.c_void_p()
+    _check(lib().tree_attn_plan_decode_paged(_ptr(P), _ptr(N), _ptr(L), int(P.size), _ptr(bp), _ptr(br), _ptr(s),
+                                             None if kq is None else _ptr(kq), int(bp.size), block_size,
+                                             n_cache_blocks, _ptr(mb), _p64(mo), _ptr(sb), _p64(so),
+                                             ctypes.byref(out)))
+    return Plan(out.value, TA_PLAN_DECODE)
+
+
+def plan_verify_paged(ctx_len, br_page, n_nodes, parent, block_size: int, n_cache_blocks: int, ctx_tables) -> Plan:
+    c, bp, nn, pa = _i32(ctx_len), _i32(br_page), _i32(n_nodes), _i32(parent)
+    cb, co = _tables(ctx_tables)
+    out = ctypes.c_void_p()
+    _check(lib().tree_attn_plan_verify_paged(_ptr(c), int(c.size), _ptr(bp), _ptr(nn), _ptr(pa), int(bp.size),
+                                             block_size, n_cache_blocks, _ptr(cb), _p64(co), ctypes.byref(out)))
+    return Plan(out.value, TA_PLAN_VERIFY)
+
+
+class KVPool:
+    """Host block pool of a paged KV cache (see tree_attn_pool_* in the header)."""
+
+    def __init__(self, n_blocks: int, block_size: int):
+        h = ctypes.c_void_p()
+        _check(lib().tree_attn_pool_create(n_blocks, block_size, ctypes.byref(h)))
+        self.handle, self.n_blocks, self.block_size = h, n_blocks, block_size
+
+    def new_seq(self) -> int:
+        s = ctypes.c_int32()
+        _check(lib().tree_attn_pool_new_seq(self.handle, ctypes.byref(s)))
+        return s.value
+
+    def fork(self, parent: int, n_tokens: int) -> int:
+        s = ctypes.c_int32()
+        _check(lib().tree_attn_pool_fork(self.handle, parent, n_tokens, ctypes.byref(s)))
+        return s.value
+
+    def append(self, seq: int, n_tokens: int) -> np.ndarray:
+        slots = np.zeros(max(n_tokens, 0), np.int64)
+        _check(lib().tree_attn_pool_append(self.handle, seq, n_tokens, _p64(slots)))
+        return slots
+
+    def release(self, seq: int):
+        _check(lib().tree_attn_pool_release(self.handle, seq))
+
+    def table(self, seq: int):
+        """(view blocks, view tokens, own blocks, own tokens)."""
+        vt, ot = ctypes.c_int32(), ctypes.c_int32()
+        rc = lib().tree_attn_pool_table(self.handle, seq, None, 0, ctypes.byref(vt), None, 0, ctypes.byref(ot))
+        if rc not in (TA_OK, TA_ERR_WORKSPACE):
+            _check(rc)
+        bs = self.block_size
+        v = np.zeros((vt.value + bs - 1) // bs, np.int32)
+        o = np.zeros((ot.value + bs - 1) // bs, np.int32)
+        _check(lib().tree_attn_pool_table(self.handle, seq, _ptr(v), v.size, ctypes.byref(vt), _ptr(o), o.size,
+                                          ctypes.byref(ot)))
+        return v, vt.value, o, ot.value
+
+    def refs(self):
+        r = np.zeros(self.n_blocks, np.int32)
+        f = ctypes.c_int32()
+        _check(lib().tree_attn_pool_refs(self.handle, _ptr(r) if r.size else None, self.n_blocks, ctypes.byref(f)))
+        return r, f.value
+
+    def close(self):
+        if self.handle:
+            lib().tree_attn_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -62,6 +62,8 @@ AttnParams base_params(const ta_plan* plan, int32_t hq, int32_t hkv, float scale
   p.row_a = reinterpret_cast<const int32_t*>(dev + plan->layout.row_a);
   p.row_b = reinterpret_cast<const int32_t*>(dev + plan->layout.row_b);
   p.row_mask = reinterpret_cast<const uint64_t*>(dev + plan->layout.mask);
+  p.tile_a = plan->tile_a.empty() ? nullptr : reinterpret_cast<const int32_t*>(dev + plan->layout.tile_a);
+  p.tile_b = plan->tile_b.empty() ? nullptr : reinterpret_cast<const int32_t*>(dev + plan->layout.tile_b);
   p.hq = hq;
   p.hkv = hkv;
   p.group = hq / hkv;
@@ -157,6 +159,12 @@ extern "C" int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t
       for (const WorkItem& w : plan->kwork)
         work_tmp.insert(work_tmp.end(), {w.row0, w.nrows, w.a_lo, w.a_full, w.a_hi, w.b_lo, w.b_hi, w.out,
                                          w.flags, w.tile_hi});
+      src = &work_tmp;
+      break;
+    case TA_FIELD_PAGED_TILES:
+      if (plan->tile_a.empty() && plan->tile_b.empty()) break;
+      work_tmp.assign(plan->tile_a.begin(), plan->tile_a.end());
+      work_tmp.insert(work_tmp.end(), plan->tile_b.begin(), plan->tile_b.end());
       src = &work_tmp;
       break;
     case TA_FIELD_WORK:

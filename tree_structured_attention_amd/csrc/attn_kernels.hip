@@ -261,15 +261,27 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   // prefill and verify re-read tiles across row tiles and keep the default
   TileLoader<T, D, NW, MODE == kDecode ? kCpolStream : 0> loader;
   loader.init(lane, wave, kv_stride);
+  // Tile `it` of this item: segment A's tiles, then B's.  Paged segments
+  // (decode and verify only) find each tile's first cache row in the plan's
+  // tile table; tiles start on 64-token boundaries of their sequence and
+  // blocks hold whole tiles.
+  const int a_lo = wi.a_lo, a_hi = wi.a_hi, b_lo = wi.b_lo, b_hi = wi.b_hi;
+  auto issue_tile = [&](unsigned char* stage, int it) {
+    const bool in_a = it < n_a;
+    const int t0 = in_a ? a_lo + it * kKeyTile : b_lo + (it - n_a) * kKeyTile;
+    const int t1 = in_a ? a_hi : b_hi;
+    const unsigned char* kbase = in_a ? ka : kb;
+    const unsigned char* vbase = in_a ? va : vb;
+    int64_t row = t0;
+    if constexpr (MODE != kPrefill) {
+      const int32_t* tiles = in_a ? p.tile_a : p.tile_b;
+      if (tiles) row = tiles[t0 / kKeyTile];
+    }
+    loader.issue_rows(stage, kbase + row * kv_stride, vbase + row * kv_stride, t1 - t0, kv_stride, wave);
+  };
   // this item's tiles: [tile_lo, tile_hi) of segment A's tiles then B's
   const int it_lo = wi.tile_lo, it_hi = min(wi.tile_hi, n_tiles);
-  if (it_lo < it_hi) {
-    unsigned char* stage = lds0;
-    if (it_lo < n_a)
-      loader.issue(stage, ka, va, wi.a_lo + it_lo * kKeyTile, wi.a_hi, kv_stride, wave);
-    else
-      loader.issue(stage, kb, vb, wi.b_lo + (it_lo - n_a) * kKeyTile, wi.b_hi, kv_stride, wave);
-  }
+  if (it_lo < it_hi) issue_tile(lds0, it_lo);
 
   RS rs;
   rs.h = lane >> 5;
@@ -316,19 +328,12 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   // Tiles alternate between two LDS buffers, so each is a distinct object:
   // the next tile's copy into one never has to complete before reads of the
   // other.
-  const int a_lo = wi.a_lo, a_hi = wi.a_hi, b_lo = wi.b_lo, b_hi = wi.b_hi;
   auto step = [&](int it, const unsigned char* cur, unsigned char* nxt) {
     // this wave's copies into `cur` are done (vmcnt(0)), then the barrier
     // publishes all of them and retires every wave's reads of `nxt`
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (it + 1 < it_hi) {
-      const int nx = it + 1;
-      if (nx < n_a)
-        loader.issue(nxt, ka, va, a_lo + nx * kKeyTile, a_hi, kv_stride, wave);
-      else
-        loader.issue(nxt, kb, vb, b_lo + (nx - n_a) * kKeyTile, b_hi, kv_stride, wave);
-    }
+    if (it + 1 < it_hi) issue_tile(nxt, it + 1);
     if (wave_active) {
       const bool seg_a = it < n_a;
       const int t0 = seg_a ? a_lo + it * kKeyTile : b_lo + (it - n_a) * kKeyTile;

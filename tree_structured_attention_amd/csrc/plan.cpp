@@ -58,6 +58,45 @@ WorkItem make_item(int64_t row0, int64_t nrows, int64_t a_lo, int64_t a_full, in
   return w;
 }
 
+// Block tables of paged plans.  A sequence i of `len(i)` tokens reads token t
+// from cache row blocks[off[i] + t / bs] * bs + t % bs.  Block sizes are
+// multiples of the 64-key tile, so no tile straddles two blocks.
+struct Paging {
+  int32_t bs = 0, n_cache_blocks = 0;
+  const int32_t* blocks = nullptr;
+  const int64_t* off = nullptr;
+  bool on() const { return bs > 0; }
+};
+
+int64_t round_tile(int64_t n) { return (n + kKeyTile - 1) / kKeyTile * kKeyTile; }
+
+int check_paging(const Paging& pg, int32_t n_seq, const std::vector<int64_t>& len, const char* who) {
+  if (pg.bs < kKeyTile || pg.bs % kKeyTile != 0)
+    return fail(TA_ERR_INVALID_ARG, std::string(who) + ": block_size must be a positive multiple of 64");
+  if (pg.n_cache_blocks < 0 || int64_t(pg.n_cache_blocks) * pg.bs >= kMax32)
+    return fail(TA_ERR_CAPACITY, std::string(who) + ": cache rows must stay below 2^31");
+  if (n_seq > 0 && (!pg.off || !pg.blocks)) return fail(TA_ERR_INVALID_ARG, std::string(who) + ": NULL block table");
+  for (int32_t i = 0; i < n_seq; ++i) {
+    const int64_t need = (len[i] + pg.bs - 1) / pg.bs;
+    if (pg.off[i] < 0 || pg.off[i + 1] - pg.off[i] < need)
+      return fail(TA_ERR_INVALID_ARG, std::string(who) + ": a block table is shorter than its sequence");
+    for (int64_t j = 0; j < need; ++j) {
+      const int32_t b = pg.blocks[pg.off[i] + j];
+      if (b < 0 || b >= pg.n_cache_blocks) return fail(TA_ERR_INVALID_ARG, std::string(who) + ": block id out of range");
+    }
+  }
+  return TA_OK;
+}
+
+// Physical row of every tile of the sequences laid out from virtual bases.
+void fill_tiles(const Paging& pg, int32_t n_seq, const std::vector<int64_t>& len, const std::vector<int64_t>& vbase,
+                int64_t v_total, std::vector<int32_t>& tiles) {
+  tiles.assign(size_t(v_total / kKeyTile), 0);
+  for (int32_t i = 0; i < n_seq; ++i)
+    for (int64_t t = 0; t < len[i]; t += kKeyTile)
+      tiles[size_t((vbase[i] + t) / kKeyTile)] = pg.blocks[pg.off[i] + t / pg.bs] * pg.bs + int32_t(t % pg.bs);
+}
+
 }  // namespace
 
 int64_t item_tiles(const WorkItem& w) {
@@ -81,6 +120,10 @@ void pack_blob(ta_plan* p) {
   off = align256(off + int64_t(p->kwork.size() * sizeof(WorkItem)));
   L.trees = off;
   off = align256(off + int64_t(p->tree_tab.size() * 4));
+  L.tile_a = off;
+  off = align256(off + int64_t(p->tile_a.size() * 4));
+  L.tile_b = off;
+  off = align256(off + int64_t(p->tile_b.size() * 4));
   L.total = std::max<int64_t>(off, 256);
   p->layout = L;
   p->blob.assign(size_t(L.total), 0);
@@ -94,6 +137,8 @@ void pack_blob(ta_plan* p) {
   put(L.merge, p->merge.data(), p->merge.size() * sizeof(MergeRow));
   put(L.kwork, p->kwork.data(), p->kwork.size() * sizeof(WorkItem));
   put(L.trees, p->tree_tab.data(), p->tree_tab.size() * 4);
+  put(L.tile_a, p->tile_a.data(), p->tile_a.size() * 4);
+  put(L.tile_b, p->tile_b.data(), p->tile_b.size() * 4);
 }
 
 }  // namespace ta
@@ -262,9 +307,12 @@ extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* 
 namespace {
 
 // Decode plan with n_query[b] new tokens per live branch (NULL: one each).
+// With paging, the pages' main streams (pa, per page) and the branches'
+// suffixes (pb, per branch) are read through block tables; their virtual
+// positions start on 64-token boundaries.
 int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int32_t* layout_len, int32_t n_pages,
                  const int32_t* br_page, const int32_t* br_region, const int32_t* suffix_len,
-                 const int32_t* n_query, int32_t n_branches, ta_plan** out) {
+                 const int32_t* n_query, int32_t n_branches, const Paging& pa, const Paging& pb, ta_plan** out) {
   if (!out) return fail(TA_ERR_INVALID_ARG, "plan_decode: out is NULL");
   if (n_pages < 0 || n_branches < 0) return fail(TA_ERR_INVALID_ARG, "plan_decode: negative count");
   if (n_pages > 0 && (!prefix_len || !n_regions))
@@ -277,13 +325,15 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
     reg_off[p + 1] = reg_off[p] + n_regions[p];
   }
   if (reg_off[n_pages] > 0 && !layout_len) return fail(TA_ERR_INVALID_ARG, "plan_decode: NULL layout_len");
+  std::vector<int64_t> page_len(static_cast<size_t>(n_pages));
   for (int32_t p = 0; p < n_pages; ++p) {
     int64_t m = prefix_len[p];
     for (int64_t r = reg_off[p]; r < reg_off[p + 1]; ++r) {
       if (layout_len[r] < 0) return fail(TA_ERR_INVALID_ARG, "plan_decode: negative layout_len");
       m += layout_len[r];
     }
-    main_off[p + 1] = main_off[p] + m;
+    page_len[p] = m;
+    main_off[p + 1] = main_off[p] + (pa.on() ? round_tile(m) : m);
     if (main_off[p + 1] >= kMax32) return fail(TA_ERR_CAPACITY, "plan_decode: main tokens >= 2^31");
   }
   auto kq = [&](int32_t b) -> int64_t { return n_query ? n_query[b] : 1; };
@@ -296,10 +346,18 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
       return fail(TA_ERR_INVALID_ARG, "plan_decode: br_region must be 0 (layout stream) or 1..N of its page");
     if (suffix_len[b] < 0) return fail(TA_ERR_INVALID_ARG, "plan_decode: negative suffix_len");
     if (kq(b) < 1) return fail(TA_ERR_INVALID_ARG, "plan_decode: n_query must be >= 1");
-    suffix_total += int64_t(suffix_len[b]) + kq(b);
+    suffix_total += pb.on() ? round_tile(int64_t(suffix_len[b]) + kq(b)) : int64_t(suffix_len[b]) + kq(b);
     rows_total += kq(b);
     if (suffix_total >= kMax32) return fail(TA_ERR_CAPACITY, "plan_decode: suffix tokens >= 2^31");
     if (rows_total >= kMax32) return fail(TA_ERR_CAPACITY, "plan_decode: query rows >= 2^31");
+  }
+
+  std::vector<int64_t> suf_len(static_cast<size_t>(n_branches));
+  for (int32_t b = 0; b < n_branches; ++b) suf_len[b] = int64_t(suffix_len[b]) + kq(b);
+  if (pa.on()) {
+    int rc = check_paging(pa, n_pages, page_len, "plan_decode_paged (main)");
+    if (!rc) rc = check_paging(pb, n_branches, suf_len, "plan_decode_paged (suffix)");
+    if (rc) return rc;
   }
 
   auto* pl = new ta_plan();
@@ -307,8 +365,8 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
   pl->n_pages = n_pages;
   pl->n_branches = n_branches;
   pl->n_rows = rows_total;
-  pl->n_keys_a = main_off[n_pages];
-  pl->n_keys_b = suffix_total;
+  pl->n_keys_a = pa.on() ? int64_t(pa.n_cache_blocks) * pa.bs : main_off[n_pages];
+  pl->n_keys_b = pb.on() ? int64_t(pb.n_cache_blocks) * pb.bs : suffix_total;
   pl->row_a.resize(size_t(rows_total));
   pl->row_b.resize(size_t(rows_total));
   pl->merge.resize(size_t(rows_total));
@@ -333,7 +391,11 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
       pl->decode_rows5.insert(pl->decode_rows5.end(), {main_off[p], m, s0, vis_suffix, m + vis_suffix - 1});
       pl->visible_pairs += m + vis_suffix;
     }
-    s0 += int64_t(suffix_len[b]) + kq(b);
+    s0 += pb.on() ? round_tile(suf_len[b]) : suf_len[b];
+  }
+  if (pa.on()) {
+    fill_tiles(pa, n_pages, page_len, main_off, main_off[n_pages], pl->tile_a);
+    fill_tiles(pb, n_branches, suf_len, suf_start, suffix_total, pl->tile_b);
   }
 
   // Pass-1 work items.  Partial slots (per query head) are numbered in plan
@@ -416,7 +478,7 @@ extern "C" int tree_attn_plan_decode(const int32_t* prefix_len, const int32_t* n
                                      const int32_t* suffix_len, int32_t n_branches,
                                      ta_plan** out) {
   return build_decode(prefix_len, n_regions, layout_len, n_pages, br_page, br_region, suffix_len, nullptr,
-                      n_branches, out);
+                      n_branches, Paging{}, Paging{}, out);
 }
 
 extern "C" int tree_attn_plan_decode_multi(const int32_t* prefix_len, const int32_t* n_regions,
@@ -426,12 +488,35 @@ extern "C" int tree_attn_plan_decode_multi(const int32_t* prefix_len, const int3
                                            int32_t n_branches, ta_plan** out) {
   if (n_branches > 0 && !n_query) return fail(TA_ERR_INVALID_ARG, "plan_decode_multi: NULL n_query");
   return build_decode(prefix_len, n_regions, layout_len, n_pages, br_page, br_region, suffix_len, n_query,
-                      n_branches, out);
+                      n_branches, Paging{}, Paging{}, out);
 }
 
-extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page,
-                                     const int32_t* n_nodes, const int32_t* parent, int32_t n_branches,
-                                     ta_plan** out) {
+extern "C" int tree_attn_plan_decode_paged(const int32_t* prefix_len, const int32_t* n_regions,
+                                           const int32_t* layout_len, int32_t n_pages,
+                                           const int32_t* br_page, const int32_t* br_region,
+                                           const int32_t* suffix_len, const int32_t* n_query,
+                                           int32_t n_branches, int32_t block_size, int32_t n_cache_blocks,
+                                           const int32_t* main_blocks, const int64_t* main_block_off,
+                                           const int32_t* suffix_blocks, const int64_t* suffix_block_off,
+                                           ta_plan** out) {
+  Paging pa, pb;
+  pa.bs = pb.bs = block_size;
+  pa.n_cache_blocks = pb.n_cache_blocks = n_cache_blocks;
+  pa.blocks = main_blocks;
+  pa.off = main_block_off;
+  pb.blocks = suffix_blocks;
+  pb.off = suffix_block_off;
+  if (block_size <= 0) return fail(TA_ERR_INVALID_ARG, "plan_decode_paged: block_size must be a positive multiple of 64");
+  return build_decode(prefix_len, n_regions, layout_len, n_pages, br_page, br_region, suffix_len, n_query,
+                      n_branches, pa, pb, out);
+}
+
+namespace {
+
+// Verify plan; with paging the pages' contexts are read through block tables
+// (virtual positions on 64-token boundaries) and tree nodes stay contiguous.
+int build_verify(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page, const int32_t* n_nodes,
+                 const int32_t* parent, int32_t n_branches, const Paging& pa, ta_plan** out) {
   if (!out) return fail(TA_ERR_INVALID_ARG, "plan_verify: out is NULL");
   if (n_pages < 0 || n_branches < 0) return fail(TA_ERR_INVALID_ARG, "plan_verify: negative count");
   if (n_pages > 0 && !ctx_len) return fail(TA_ERR_INVALID_ARG, "plan_verify: NULL ctx_len");
@@ -439,7 +524,7 @@ extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, co
   std::vector<int64_t> ctx_off(size_t(n_pages) + 1, 0);
   for (int32_t p = 0; p < n_pages; ++p) {
     if (ctx_len[p] < 0) return fail(TA_ERR_INVALID_ARG, "plan_verify: negative ctx_len");
-    ctx_off[p + 1] = ctx_off[p] + ctx_len[p];
+    ctx_off[p + 1] = ctx_off[p] + (pa.on() ? round_tile(ctx_len[p]) : ctx_len[p]);
     if (ctx_off[p + 1] >= kMax32) return fail(TA_ERR_CAPACITY, "plan_verify: context tokens >= 2^31");
   }
   int64_t total_nodes = 0;
@@ -465,13 +550,21 @@ extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, co
     }
   }
 
+  std::vector<int64_t> clen(static_cast<size_t>(n_pages));
+  for (int32_t p = 0; p < n_pages; ++p) clen[p] = ctx_len[p];
+  if (pa.on()) {
+    const int rc = check_paging(pa, n_pages, clen, "plan_verify_paged");
+    if (rc) return rc;
+  }
+
   auto* pl = new ta_plan();
   pl->kind = TA_PLAN_VERIFY;
   pl->n_pages = n_pages;
   pl->n_branches = n_branches;
   pl->n_rows = total_nodes;
-  pl->n_keys_a = ctx_off[n_pages];
+  pl->n_keys_a = pa.on() ? int64_t(pa.n_cache_blocks) * pa.bs : ctx_off[n_pages];
   pl->n_keys_b = total_nodes;
+  if (pa.on()) fill_tiles(pa, n_pages, clen, ctx_off, ctx_off[n_pages], pl->tile_a);
   pl->row_a.resize(size_t(total_nodes));
   pl->row_b.resize(size_t(total_nodes));
   pl->row_mask.resize(size_t(total_nodes));
@@ -491,7 +584,7 @@ extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, co
       bits[i] = (pa < 0 ? 0ull : bits[pa]) | (1ull << i);
       dep[i] = pa < 0 ? 0 : dep[pa] + 1;
       const int64_t row = node_off[b] + i;
-      pl->row_a[row] = int32_t(ctx_off[p + 1]);
+      pl->row_a[row] = int32_t(ctx_off[p] + ctx_len[p]);
       pl->row_b[row] = int32_t(node_off[b]);
       pl->row_mask[row] = bits[i];
       pl->verify_mask[row] = int64_t(bits[i]);
@@ -508,7 +601,7 @@ extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, co
     int64_t nodes = 0;
     while (e < n_branches && br_page[e] == p && nodes + n_nodes[e] <= kTileTokens) nodes += n_nodes[e++];
     if (nodes > 0) {
-      pl->work.push_back(make_item(node_off[b], nodes, ctx_off[p], ctx_off[p + 1], ctx_off[p + 1],
+      pl->work.push_back(make_item(node_off[b], nodes, ctx_off[p], ctx_off[p] + ctx_len[p], ctx_off[p] + ctx_len[p],
                                    node_off[b], node_off[e], -1, 0));
     }
     b = e;
@@ -517,6 +610,27 @@ extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, co
   pack_blob(pl);
   *out = pl;
   return TA_OK;
+}
+
+}  // namespace
+
+extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page,
+                                     const int32_t* n_nodes, const int32_t* parent, int32_t n_branches,
+                                     ta_plan** out) {
+  return build_verify(ctx_len, n_pages, br_page, n_nodes, parent, n_branches, Paging{}, out);
+}
+
+extern "C" int tree_attn_plan_verify_paged(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page,
+                                           const int32_t* n_nodes, const int32_t* parent, int32_t n_branches,
+                                           int32_t block_size, int32_t n_cache_blocks, const int32_t* ctx_blocks,
+                                           const int64_t* ctx_block_off, ta_plan** out) {
+  Paging pa;
+  pa.bs = block_size;
+  pa.n_cache_blocks = n_cache_blocks;
+  pa.blocks = ctx_blocks;
+  pa.off = ctx_block_off;
+  if (block_size <= 0) return fail(TA_ERR_INVALID_ARG, "plan_verify_paged: block_size must be a positive multiple of 64");
+  return build_verify(ctx_len, n_pages, br_page, n_nodes, parent, n_branches, pa, out);
 }
 
 namespace {

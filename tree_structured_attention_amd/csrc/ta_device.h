@@ -113,14 +113,20 @@ struct TileLoader {
     }
   }
 
+  // rows [t0, min(t1, t0 + 64)) of a contiguous segment
   __device__ __forceinline__ void issue(unsigned char* stage, const unsigned char* kbase, const unsigned char* vbase,
                                         int t0, int t1, int64_t row_stride, int wave) const {
-    const int rows = min(t1 - t0, kKeyTile);
+    issue_rows(stage, kbase + int64_t(t0) * row_stride, vbase + int64_t(t0) * row_stride, t1 - t0, row_stride, wave);
+  }
+  // min(rows, 64) rows starting at the given K and V rows
+  __device__ __forceinline__ void issue_rows(unsigned char* stage, const unsigned char* krow, const unsigned char* vrow,
+                                             int rows, int64_t row_stride, int wave) const {
+    rows = min(rows, kKeyTile);
     const int nbytes = rows > 0 ? int(rows * row_stride) : 0;
     __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(kbase) + int64_t(t0) * row_stride, (short)0, nbytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(krow), (short)0, nbytes, 0x00020000);
     __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vbase) + int64_t(t0) * row_stride, (short)0, nbytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(vrow), (short)0, nbytes, 0x00020000);
 #pragma unroll
     for (int j = 0; j < kInsts; ++j) {
       const int row0 = (j * NW + wave) * kRowsPerInst;

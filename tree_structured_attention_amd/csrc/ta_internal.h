@@ -62,7 +62,8 @@ static_assert(sizeof(MergeRow) == 32, "merge row layout");
 
 // Offsets (bytes) of the tables inside the device workspace.
 struct DeviceLayout {
-  int64_t work = 0, row_a = 0, row_b = 0, mask = 0, merge = 0, kwork = 0, trees = 0, total = 0;
+  int64_t work = 0, row_a = 0, row_b = 0, mask = 0, merge = 0, kwork = 0, trees = 0, tile_a = 0, tile_b = 0,
+          total = 0;
 };
 
 }  // namespace ta
@@ -85,6 +86,10 @@ struct ta_plan {
   std::vector<ta::MergeRow> merge;
   std::vector<ta::WorkItem> kwork;  // prefill: key-major items of the backward
   std::vector<int32_t> tree_tab;    // verify: node offsets [n_branches + 1], then parents [n_rows]
+  // paged plans: physical cache row of the first token of every 64-token
+  // tile of segment A / segment B, indexed by virtual position / 64 (empty
+  // when that segment is contiguous)
+  std::vector<int32_t> tile_a, tile_b;
   ta::DeviceLayout layout;
   std::vector<unsigned char> blob;  // packed image of the device tables
 

@@ -25,6 +25,10 @@ struct AttnParams {
   const int32_t* row_a;
   const int32_t* row_b;
   const uint64_t* row_mask;
+  // paged plans: cache row of the first token of each 64-token tile of
+  // segment A / B, by virtual position / 64; NULL for a contiguous segment
+  const int32_t* tile_a;
+  const int32_t* tile_b;
   int32_t hq, hkv, group;
   float c;  // softmax scale * log2(e)
   int64_t n_rows;
