@@ -11,8 +11,9 @@ inputs:
 The prefill backward (dq, dk, dv of the same page), the greedy acceptance
 walk over the verify trees (bf16 logits, 151,936-entry vocabulary) and a
 multi-token decode (8-token windows for the decode pages' 24 branches plus
-one layout-stream row per page) are timed in the same loop and reported
-under entries, outside the step.
+one layout-stream row per page) and the decode workload read from a paged
+cache of 64-token blocks are timed in the same loop and reported under
+entries, outside the step.
 Each entry point is bracketed by HIP events on the stream it is launched on
 (torch's current stream).  The single JSON line on stdout reports prefill
 packed tokens/s as `value`, with decode and verify beside it, a roofline per
@@ -104,6 +105,62 @@ def decode_case(w=None, name="decode"):
     return dict(name=name, w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="query tokens",
                 flops=flops, bytes=kv_bytes + qo_bytes, bound="hbm", plan_us=plan_us, in_step=name == "decode",
                 kernel="attn_kernel<bf16,128,2,decode> + merge_kernel")
+
+
+def decode_paged_case():
+    """The decode workload with every main stream and suffix in a paged cache
+    of 64-token blocks from the host pool (branches fork their page's main
+    stream without copying it): timed beside the step."""
+    w = synth.config4()
+    desc, t = w.desc, w.tensors
+    bs = 64
+    main = desc.main_tokens()
+    suf = desc.suffix_len.astype(np.int64) + desc.queries()
+    nb = int(sum((int(m) + bs - 1) // bs for m in main) + sum((int(s) + bs - 1) // bs for s in suf)) + 64
+    pool = ta.KVPool(nb, bs)
+    reg_off = np.concatenate([[0], np.cumsum(desc.n_regions.astype(np.int64))])
+    m_off = np.concatenate([[0], np.cumsum(main)])
+    s_off = np.concatenate([[0], np.cumsum(suf)])
+    roots, slots_k = [], []
+    ck = torch.zeros((nb * bs,) + tuple(t["k_main"].shape[1:]), dtype=t["k_main"].dtype, device="cuda")
+    cv = torch.zeros_like(ck)
+    for p in range(desc.n_pages):
+        r = pool.new_seq()
+        s = torch.as_tensor(pool.append(r, int(main[p])), device="cuda")
+        ck[s] = t["k_main"][m_off[p]:m_off[p + 1]].cuda()
+        cv[s] = t["v_main"][m_off[p]:m_off[p + 1]].cuda()
+        roots.append(r)
+    st = []
+    t0 = time.perf_counter()
+    for b in range(desc.n_branches):
+        p = int(desc.br_page[b])
+        k = int(desc.br_region[b]) or int(desc.n_regions[p])
+        bound = int(desc.prefix_len[p]) + int(desc.layout_len[reg_off[p]:reg_off[p] + k].sum())
+        c = pool.fork(roots[p], bound)
+        s = torch.as_tensor(pool.append(c, int(suf[b])), device="cuda")
+        ck[s] = t["k_suffix"][s_off[b]:s_off[b + 1]].cuda()
+        cv[s] = t["v_suffix"][s_off[b]:s_off[b + 1]].cuda()
+        st.append(pool.table(c)[2])
+    mt = [pool.table(r)[2] for r in roots]
+    plan = ta.plan_decode_paged(desc.prefix_len, desc.n_regions, desc.layout_len, desc.br_page, desc.br_region,
+                                desc.suffix_len, None, bs, nb, mt, st)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    plan.upload()
+    q = t["q"].cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.hq, q.shape[0]), dtype=torch.float32, device="cuda")
+    scratch = scratch_for(plan, w)
+    info = plan.info
+
+    def run():
+        ta.decode(plan, q, ck, cv, ck, cv, scale=w.scale, out=o, lse=lse, scratch=scratch)
+
+    e = elt(w.dtype)
+    kv_bytes = (int(main.sum()) + int(suf.sum())) * w.hkv * w.head_dim * 2 * e
+    qo_bytes = info["n_rows"] * w.hq * w.head_dim * 2 * e + info["n_rows"] * w.hq * 4
+    return dict(name="decode_paged", w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="query tokens",
+                flops=4.0 * w.head_dim * w.hq * info["visible_pairs"], bytes=kv_bytes + qo_bytes, bound="hbm",
+                plan_us=plan_us, in_step=False, kernel="attn_kernel<bf16,128,2,decode> + merge_kernel (paged)")
 
 
 def decode_multi_case():
@@ -258,7 +315,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward", "accept", "decode_multi"],
+    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward", "accept", "decode_multi",
+                                       "decode_paged"],
                     default=None,
                     help="time one entry point only (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -284,7 +342,8 @@ def main():
     log("[bench] generating inputs")
     cases = []
     for name, fn in (("prefill", prefill_case), ("decode", decode_case), ("verify", verify_case),
-                     ("backward", backward_case), ("accept", accept_case), ("decode_multi", decode_multi_case)):
+                     ("backward", backward_case), ("accept", accept_case), ("decode_multi", decode_multi_case),
+                     ("decode_paged", decode_paged_case)):
         if args.only is None or args.only == name:
             cases.append(fn())
             log(f"[bench] {name}: {cases[-1]['w'].name} ready")
@@ -366,6 +425,8 @@ def main():
         out["accept_hbm_frac"] = per_case["accept"]["roofline"]["frac"]
     if "decode_multi" in per_case:
         out["decode_multi_hbm_frac"] = per_case["decode_multi"]["roofline"]["frac"]
+    if "decode_paged" in per_case:
+        out["decode_paged_hbm_frac"] = per_case["decode_paged"]["roofline"]["frac"]
     if not args.no_cpu_baseline and args.only is None:
         log("[bench] timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
