@@ -130,21 +130,25 @@ def decode_paged_case():
         ck[s] = t["k_main"][m_off[p]:m_off[p + 1]].cuda()
         cv[s] = t["v_main"][m_off[p]:m_off[p + 1]].cuda()
         roots.append(r)
-    st = []
+    # host cost of a step's bookkeeping: fork every branch, give it room for
+    # its suffix, build the paged plan
+    st, suffix_slots = [], []
     t0 = time.perf_counter()
     for b in range(desc.n_branches):
         p = int(desc.br_page[b])
         k = int(desc.br_region[b]) or int(desc.n_regions[p])
         bound = int(desc.prefix_len[p]) + int(desc.layout_len[reg_off[p]:reg_off[p] + k].sum())
         c = pool.fork(roots[p], bound)
-        s = torch.as_tensor(pool.append(c, int(suf[b])), device="cuda")
-        ck[s] = t["k_suffix"][s_off[b]:s_off[b + 1]].cuda()
-        cv[s] = t["v_suffix"][s_off[b]:s_off[b + 1]].cuda()
+        suffix_slots.append(pool.append(c, int(suf[b])))
         st.append(pool.table(c)[2])
     mt = [pool.table(r)[2] for r in roots]
     plan = ta.plan_decode_paged(desc.prefix_len, desc.n_regions, desc.layout_len, desc.br_page, desc.br_region,
                                 desc.suffix_len, None, bs, nb, mt, st)
     plan_us = (time.perf_counter() - t0) * 1e6
+    for b in range(desc.n_branches):
+        s = torch.as_tensor(suffix_slots[b], device="cuda")
+        ck[s] = t["k_suffix"][s_off[b]:s_off[b + 1]].cuda()
+        cv[s] = t["v_suffix"][s_off[b]:s_off[b + 1]].cuda()
     plan.upload()
     q = t["q"].cuda()
     o = torch.empty_like(q)
