@@ -398,6 +398,29 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
     fill_tiles(pb, n_branches, suf_len, suf_start, suffix_total, pl->tile_b);
   }
 
+  // Chunk length: the longest (down to kDecodeChunkMin) that keeps at least
+  // kDecodeMinItems pass-1 items.
+  auto n_items = [&](int64_t chunk) {
+    int64_t n = 0;
+    for (int32_t b0 = 0, e0; b0 < n_branches; b0 = e0) {
+      e0 = b0;
+      while (e0 < n_branches && br_page[e0] == br_page[b0]) ++e0;
+      for (int64_t g0 = row_off[b0]; g0 < row_off[e0]; g0 += kTileTokens) {
+        int64_t hi = 0;
+        for (int64_t i = g0; i < std::min(row_off[e0], g0 + kTileTokens); ++i) hi = std::max(hi, main_len[i]);
+        n += (hi + chunk - 1) / chunk;
+      }
+    }
+    for (int32_t i = 0; i < n_branches; ++i)
+      for (int64_t j0 = 0; j0 < kq(i); j0 += kTileTokens) {
+        const int64_t len = int64_t(suffix_len[i]) + std::min(kq(i), j0 + kTileTokens);
+        n += len <= kDecodeSuffixWhole ? 1 : (len + chunk - 1) / chunk;
+      }
+    return n;
+  };
+  int64_t dchunk = kDecodeChunkMax;
+  while (dchunk > kDecodeChunkMin && n_items(dchunk) < kDecodeMinItems) dchunk /= 2;
+
   // Pass-1 work items.  Partial slots (per query head) are numbered in plan
   // order: a shared chunk owns one slot per row of its row group, and so does
   // a suffix chunk.
@@ -415,10 +438,10 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
         hi = std::max(hi, main_len[i]);
         lo_bound = std::min(lo_bound, main_len[i]);
       }
-      const int64_t n_chunks = (hi + kDecodeChunk - 1) / kDecodeChunk;
+      const int64_t n_chunks = (hi + dchunk - 1) / dchunk;
       const int64_t first = slot;
       for (int64_t c = 0; c < n_chunks; ++c) {
-        const int64_t c0 = c * kDecodeChunk, c1 = std::min(hi, c0 + kDecodeChunk);
+        const int64_t c0 = c * dchunk, c1 = std::min(hi, c0 + dchunk);
         pl->work.push_back(make_item(g0, g1 - g0, main_off[p] + c0, main_off[p] + lo_bound, main_off[p] + c1,
                                      0, 0, slot, 0));
         slot += g1 - g0;
@@ -427,7 +450,7 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
         MergeRow& mr = pl->merge[i];
         mr.row = int32_t(i);
         mr.sh_first = int32_t(first + (i - g0));
-        mr.sh_count = int32_t((main_len[i] + kDecodeChunk - 1) / kDecodeChunk);
+        mr.sh_count = int32_t((main_len[i] + dchunk - 1) / dchunk);
         mr.sh_stride = int32_t(g1 - g0);
       }
     }
@@ -441,7 +464,7 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
       const int64_t j1 = std::min(kq(i), j0 + kTileTokens);
       const int64_t len = s + j1;             // keys the group's last row sees
       const int64_t full = suf_start[i] + s + j0 + 1;  // keys every row of the group sees end here
-      const int64_t chunk = len <= kDecodeSuffixWhole ? len : kDecodeChunk;
+      const int64_t chunk = len <= kDecodeSuffixWhole ? len : dchunk;
       const int64_t n_chunks = (len + chunk - 1) / chunk;
       const int64_t first = slot;
       for (int64_t c = 0; c < n_chunks; ++c) {

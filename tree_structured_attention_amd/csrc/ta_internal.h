@@ -14,9 +14,14 @@ namespace ta {
 constexpr int kTileTokens = 64;
 // Keys per LDS tile.
 constexpr int kKeyTile = 64;
-// Decode splits a page's main stream (and long suffixes) into chunks of
-// this many keys; each chunk is one work item producing fp32 partials.
-constexpr int kDecodeChunk = 1024;
+// Decode splits a page's main stream (and long suffixes) into chunks; each
+// chunk is one work item producing fp32 partials.  Chunks are as long as
+// possible (fewer partials to write and merge) while the launch keeps at
+// least kDecodeMinItems items: the longest chunk that achieves that, halving
+// from kDecodeChunkMax down to kDecodeChunkMin.
+constexpr int kDecodeChunkMax = 8192;
+constexpr int kDecodeChunkMin = 1024;
+constexpr int kDecodeMinItems = 256;
 // Suffixes up to this length stay in one work item.
 constexpr int kDecodeSuffixWhole = 2048;
 
