@@ -266,22 +266,22 @@ def accept_case():
                 kernel="row_argmax_kernel<bf16> + tree_walk_kernel<bf16>")
 
 
-def traffic_for(kernel_name):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if
-    they were taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "tree_structured_attention_amd", "csrc", "attn_kernels.hip")
+def traffic_for(entry):
+    """HBM bytes per launch of an entry point's kernels, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current
+    kernel sources (else None)."""
     try:
-        with open(path) as f:
-            rec = json.load(f)
-        with open(src, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
-    except (OSError, ValueError):
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)["entries"][entry]
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, "tree_structured_attention_amd", "csrc", src), "rb") as f:
+                h.update(f.read())
+    except (OSError, ValueError, KeyError):
         return None
-    if rec.get("kernel_source_sha256") != digest:
+    if rec.get("source_sha256") != h.hexdigest():
         return None
-    entry = rec.get("kernels", {}).get(kernel_name)
-    return None if entry is None else entry.get("bytes_per_launch")
+    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(budget_s: float):
