@@ -118,3 +118,37 @@ def test_paged_verify_bit_identical(bs):
     o_c, lse_c = ta.verify(plan_c, q, t["k_ctx"].cuda(), t["v_ctx"].cuda(), kt, vt, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(o, o_c) and torch.equal(lse, lse_c)
+
+
+def test_paged_verify_balanced_bit_identical():
+    """A paged verify plan balanced into split row tiles (pieces start on tile
+    boundaries of the paged context) equals the contiguous plan balanced the
+    same way."""
+    w = synth.config5(n_pages=3)
+    desc, t = w.desc, w.tensors
+    bs = 128
+    pool = ta.KVPool(sum((int(c) + bs - 1) // bs for c in desc.ctx_len) + 4, bs)
+    junk = pool.new_seq()
+    pool.append(junk, 2 * bs)
+    roots, slots = [], []
+    for p in range(desc.n_pages):
+        r = pool.new_seq()
+        slots.append(pool.append(r, int(desc.ctx_len[p])))
+        roots.append(r)
+    pool.release(junk)
+    tables = [pool.table(r)[2] for r in roots]
+    c_off = np.concatenate([[0], np.cumsum(desc.ctx_len.astype(np.int64))])
+    nb = pool.n_blocks
+    ck = to_cache(nb, bs, [(slots[p], t["k_ctx"][c_off[p]:c_off[p + 1]]) for p in range(desc.n_pages)], t["k_ctx"])
+    cv = to_cache(nb, bs, [(slots[p], t["v_ctx"][c_off[p]:c_off[p + 1]]) for p in range(desc.n_pages)], t["v_ctx"])
+    plan = ta.plan_verify_paged(desc.ctx_len, desc.br_page, desc.n_nodes, desc.parent, bs, nb, tables)
+    plan.balance(w.hkv, 256)
+    plan_c = ta.plan_for(desc).balance(w.hkv, 256)
+    assert plan.info["n_partials"] > 0 and plan.info["n_partials"] == plan_c.info["n_partials"]
+    plan.upload()
+    plan_c.upload()
+    q, kt, vt = t["q"].cuda(), t["k_tree"].cuda(), t["v_tree"].cuda()
+    o, lse = ta.verify(plan, q, ck, cv, kt, vt, scale=w.scale)
+    o_c, lse_c = ta.verify(plan_c, q, t["k_ctx"].cuda(), t["v_ctx"].cuda(), kt, vt, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_c) and torch.equal(lse, lse_c)
