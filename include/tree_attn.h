@@ -14,11 +14,13 @@
  *
  * Conventions shared by every call.
  *  - Status: every int-returning call returns TA_OK or a negative TA_ERR_*.
- *    On error nothing is enqueued, no output is written, and
- *    tree_attn_last_error() (thread-local) explains.  No exception crosses
- *    the ABI.
+ *    On error nothing is enqueued, no output is written (except the sizes
+ *    tree_attn_plan_export and tree_attn_pool_table report along with
+ *    TA_ERR_WORKSPACE), and tree_attn_last_error() (thread-local) explains.
+ *    No exception crosses the ABI.
  *  - Memory: the caller allocates all device memory (tensors, plan workspace,
- *    scratch).  The library allocates only host memory for plans.
+ *    scratch, paged caches).  The library allocates only host memory for
+ *    plans and block pools.
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = default
  *    stream).  Calls only enqueue; none synchronizes the host except
  *    tree_attn_plan_destroy (waits for the plan's pending upload).  Device
