@@ -29,8 +29,8 @@ constexpr int64_t kMax32 = INT32_MAX;
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 int64_t item_cost(const WorkItem& w) {
-  const int64_t tiles = w.tile_hi - w.tile_lo;
-  return int64_t(w.nrows) * (tiles * kKeyTile + 16);
+  // a workgroup's time follows its tiles, whatever its row count
+  return int64_t(w.tile_hi - w.tile_lo) * 64 + w.nrows;
 }
 
 // Longest first, so that the long tiles start early and the short ones fill
