@@ -209,8 +209,10 @@ extern "C" int tree_attn_plan_upload(ta_plan* plan, void* dev_workspace, size_t 
 extern "C" void tree_attn_plan_destroy(ta_plan* plan) {
   if (!plan) return;
   if (plan->upload_event) {
-    hipEventSynchronize(static_cast<hipEvent_t>(plan->upload_event));
-    hipEventDestroy(static_cast<hipEvent_t>(plan->upload_event));
+    // nothing to report from a destructor: a failed wait or release leaves
+    // the error for the caller's next HIP call
+    (void)hipEventSynchronize(static_cast<hipEvent_t>(plan->upload_event));
+    (void)hipEventDestroy(static_cast<hipEvent_t>(plan->upload_event));
   }
   delete plan;
 }
