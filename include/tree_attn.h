@@ -80,8 +80,11 @@ extern "C" {
 #define TA_FIELD_PAGED_TILES 11 /* paged: [tiles of A, then tiles of B] cache row of the first token of each
                                    64-token tile, by virtual position / 64 (A: main streams or contexts; B: decode
                                    suffixes, absent for verify) */
-#define TA_FIELD_WORK 9         /* any:     [work][10] the launch work list: row0, nrows, a_lo, a_full, a_hi, b_lo, b_hi,
-                                           partial slot (-1: direct), tile_lo, tile_hi (diagnostic; order is not contractual) */
+#define TA_FIELD_WORK 9         /* any:     [work][11] the launch work list: row0, nrows, a_lo, a_full, a_hi, b_lo, b_hi,
+                                           partial slot (-1: direct), tile_lo, tile_hi, flags (1: segment B visible to
+                                           every row; decode: 4 / 8: segment A / B also read by other items, so its
+                                           copies keep the default cache policy) (diagnostic; order is not
+                                           contractual) */
 
 typedef struct ta_plan ta_plan; /* opaque, host-owned, immutable once built */
 

@@ -366,3 +366,40 @@ def test_balance_errors():
     expect(ta.TA_ERR_STATE, ta.plan_balance, plan, 8, 512)
     d = ta.plan_decode([10], [1], [1], [0], [1], [3])
     d.balance(8, 512)           # no-op for decode
+
+
+def test_decode_items_mark_segments_that_several_row_groups_read():
+    """Decode copies stream past the caches unless other items read the same
+    keys: a page with more than one row group marks its main chunks (flag 4),
+    a branch with more than one group of new tokens its suffix chunks (8)."""
+    # page 0: 3 branches x 30 new tokens = 90 rows (two row groups);
+    # page 1: branch 3 has 70 new tokens (two groups of rows and of suffix keys);
+    # page 2: two single-token branches (one group, nothing shared)
+    desc = synth.DecodeDesc(np.array([500, 300, 200], np.int32), np.array([2, 2, 1], np.int32),
+                            np.array([20, 30, 10, 10, 7], np.int32),
+                            np.array([0, 0, 0, 1, 1, 2, 2], np.int32), np.array([0, 1, 2, 1, 2, 0, 1], np.int32),
+                            np.array([40, 50, 0, 90, 5, 3, 9], np.int32),
+                            n_query=np.array([30, 30, 30, 70, 1, 1, 1], np.int32))
+    plan = ta.plan_for(desc)
+    check_decode_items(plan, desc)
+    work = plan.export("work")
+    row_page = np.repeat(desc.br_page, desc.n_query)
+    row_branch = np.repeat(np.arange(len(desc.br_page)), desc.n_query)
+    seen = set()
+    for w in work:
+        r0, nr, a_lo, a_hi, b_lo, b_hi, flags = (int(w[i]) for i in (0, 1, 2, 4, 5, 6, 10))
+        if a_hi > a_lo:
+            page = int(row_page[r0])
+            assert bool(flags & 4) == (page < 2), (page, flags)
+            seen.add(("main", page))
+        else:
+            assert b_hi > b_lo
+            br = int(row_branch[r0])
+            assert bool(flags & 8) == (br == 3), (br, flags)
+            seen.add(("suffix", br))
+        assert not flags & ~(1 | 4 | 8)
+    assert {("main", 0), ("main", 1), ("main", 2), ("suffix", 3), ("suffix", 4), ("suffix", 6)} <= seen
+    # the single-token decode workload: nothing is marked
+    w1 = synth.config4(with_tensors=False)
+    for w in ta.plan_for(w1.desc).export("work"):
+        assert int(w[10]) & (4 | 8) == 0

@@ -170,7 +170,7 @@ extern "C" int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t
     case TA_FIELD_WORK:
       for (const WorkItem& w : plan->work)
         work_tmp.insert(work_tmp.end(), {w.row0, w.nrows, w.a_lo, w.a_full, w.a_hi, w.b_lo, w.b_hi, w.out,
-                                         w.tile_lo, w.tile_hi});
+                                         w.tile_lo, w.tile_hi, w.flags});
       src = &work_tmp;
       break;
     default: break;

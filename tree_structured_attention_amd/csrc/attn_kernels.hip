@@ -256,10 +256,12 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   const unsigned char* kb = reinterpret_cast<const unsigned char*>(p.kb) + head_off;
   const unsigned char* vb = reinterpret_cast<const unsigned char*>(p.vb) + head_off;
 
-  // decode reads each K/V line once (a page's main stream is walked once for
-  // all of its branches and heads), so its copies bypass cache retention;
+  // decode reads most K/V lines once (a page's main stream is walked once for
+  // all of its branches and heads), so its copies bypass cache retention
+  // unless the item marks the segment as read by other row groups too;
   // prefill and verify re-read tiles across row tiles and keep the default
   TileLoader<T, D, NW, MODE == kDecode ? kCpolStream : 0> loader;
+  const int32_t shared_segs = MODE == kDecode ? wi.flags & (kSegAShared | kSegBShared) : 0;
   loader.init(lane, wave, kv_stride);
   // Tile `it` of this item: segment A's tiles, then B's.  Paged segments
   // (decode and verify only) find each tile's first cache row in the plan's
@@ -277,7 +279,10 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
       const int32_t* tiles = in_a ? p.tile_a : p.tile_b;
       if (tiles) row = tiles[t0 / kKeyTile];
     }
-    loader.issue_rows(stage, kbase + row * kv_stride, vbase + row * kv_stride, t1 - t0, kv_stride, wave);
+    if (shared_segs & (in_a ? kSegAShared : kSegBShared))
+      loader.template issue_rows<0>(stage, kbase + row * kv_stride, vbase + row * kv_stride, t1 - t0, kv_stride, wave);
+    else
+      loader.issue_rows(stage, kbase + row * kv_stride, vbase + row * kv_stride, t1 - t0, kv_stride, wave);
   };
   // this item's tiles: [tile_lo, tile_hi) of segment A's tiles then B's
   const int it_lo = wi.tile_lo, it_hi = min(wi.tile_hi, n_tiles);

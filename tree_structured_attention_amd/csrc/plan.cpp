@@ -430,7 +430,9 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
     const int32_t p = br_page[b];
     int32_t e = b;
     while (e < n_branches && br_page[e] == p) ++e;
-    // row groups of at most one tile of the page's rows
+    // row groups of at most one tile of the page's rows; with more than one
+    // group, every group walks the page's main stream
+    const int32_t a_shared = row_off[e] - row_off[b] > kTileTokens ? kSegAShared : 0;
     for (int64_t g0 = row_off[b]; g0 < row_off[e]; g0 += kTileTokens) {
       const int64_t g1 = std::min(row_off[e], g0 + kTileTokens);
       int64_t hi = 0, lo_bound = INT64_MAX;
@@ -443,7 +445,7 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
       for (int64_t c = 0; c < n_chunks; ++c) {
         const int64_t c0 = c * dchunk, c1 = std::min(hi, c0 + dchunk);
         pl->work.push_back(make_item(g0, g1 - g0, main_off[p] + c0, main_off[p] + lo_bound, main_off[p] + c1,
-                                     0, 0, slot, 0));
+                                     0, 0, slot, a_shared));
         slot += g1 - g0;
       }
       for (int64_t i = g0; i < g1; ++i) {
@@ -469,7 +471,8 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
       const int64_t first = slot;
       for (int64_t c = 0; c < n_chunks; ++c) {
         const int64_t c0 = suf_start[i] + c * chunk, c1 = std::min(suf_start[i] + len, c0 + chunk);
-        WorkItem w = make_item(row_off[i] + j0, j1 - j0, 0, 0, 0, c0, c1, slot, c1 <= full ? kSegBFull : 0);
+        const int32_t flags = (c1 <= full ? kSegBFull : 0) | (kq(i) > kTileTokens ? kSegBShared : 0);
+        WorkItem w = make_item(row_off[i] + j0, j1 - j0, 0, 0, 0, c0, c1, slot, flags);
         w.b_full = int32_t(std::max(c0, std::min(c1, full)));
         pl->work.push_back(w);
         slot += j1 - j0;

@@ -118,7 +118,8 @@ struct TileLoader {
                                         int t0, int t1, int64_t row_stride, int wave) const {
     issue_rows(stage, kbase + int64_t(t0) * row_stride, vbase + int64_t(t0) * row_stride, t1 - t0, row_stride, wave);
   }
-  // min(rows, 64) rows starting at the given K and V rows
+  // min(rows, 64) rows starting at the given K and V rows, with cache policy CP
+  template <int CP = CPOL>
   __device__ __forceinline__ void issue_rows(unsigned char* stage, const unsigned char* krow, const unsigned char* vrow,
                                              int rows, int64_t row_stride, int wave) const {
     rows = min(rows, kKeyTile);
@@ -130,9 +131,9 @@ struct TileLoader {
 #pragma unroll
     for (int j = 0; j < kInsts; ++j) {
       const int row0 = (j * NW + wave) * kRowsPerInst;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + row0 * G::kRowBytes), 16, voff[j], 0, 0, CPOL);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + row0 * G::kRowBytes), 16, voff[j], 0, 0, CP);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + G::kTileBytes + row0 * G::kRowBytes), 16,
-                                               voff[j], 0, 0, CPOL);
+                                               voff[j], 0, 0, CP);
     }
   }
 };

@@ -35,7 +35,10 @@ constexpr int kDecodeSuffixWhole = 2048;
 //         segment visible to all of them).
 //   out   first partial slot of the tile (per query head) when the item
 //         writes fp32 partials (decode; split prefill/verify pieces); else -1.
-//   flags bit 0: seg B fully visible.
+//   flags bit 0: seg B fully visible; bits 2 and 3 (decode): seg A / seg B
+//         is also read by other items (several row groups of a page or of a
+//         branch), so its copies keep the default cache policy instead of
+//         streaming past the caches.
 //   [tile_lo, tile_hi) the 64-key tiles (segment A's, then segment B's) this
 //         item walks; a prefill/verify row tile split for load balance has
 //         one item per piece.
@@ -45,6 +48,8 @@ struct WorkItem {
 };
 static_assert(sizeof(WorkItem) == 48, "work item layout");
 constexpr int32_t kSegBFull = 1;
+constexpr int32_t kSegAShared = 4;
+constexpr int32_t kSegBShared = 8;
 // Key-major work items of the prefill backward (dK, dV) reuse WorkItem:
 //   keys  [row0, row0 + nrows) one 64-key tile of a page's main stream or
 //         of its branch area; flags bit 1 set for the branch area
