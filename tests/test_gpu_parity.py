@@ -444,3 +444,74 @@ def test_verify_split_tiles_match_oracle():
     ro, rl = oracle.verify(w.desc, t["q"], t["k_ctx"], t["v_ctx"], t["k_tree"], t["v_tree"], w.scale)
     close(o, ro, TOL[w.dtype], "split verify o")
     close(lse, rl, LSE_TOL[w.dtype], "split verify lse")
+
+
+# --------------------------------------------------------------------------
+# score range: a row's exp2 base may lag its running maximum; tiles whose
+# scores rise far above it (up to overflowing exp2) must move it, tiles far
+# below it must not lose it
+# --------------------------------------------------------------------------
+
+def scale_keys(k, kind):
+    """Key rows times a factor of their position: 'rise' (scores grow along
+    the stream, the last tiles some hundred binary orders above the first),
+    'fall' (the reverse) or 'spike' (one stretch of keys 40 times larger)."""
+    n = k.shape[0]
+    pos = torch.arange(n, dtype=torch.float32)
+    if kind == "rise":
+        f = 1 + pos / 8
+    elif kind == "fall":
+        f = 1 + (n - 1 - pos) / 8
+    else:
+        f = torch.ones(n)
+        f[n // 3:n // 3 + 20] = 40.0
+    return (k.float() * f[:, None, None]).to(k.dtype)
+
+
+def fp32_score_tol(q, k, v, scale):
+    """fp32 inputs: the kernel's scores carry fp32 rounding of about
+    sqrt(d) * 2^-24 * scale * sum|q_i k_i| (a property of fp32 dot products,
+    not of the kernel), which perturbs every softmax weight by that relative
+    amount and the output by up to twice it times max|v|.  At scores of a few
+    hundred this passes the fixed 1e-5, so these cases widen the absolute
+    term by that bound."""
+    qa, ka = q.abs().double(), k.abs().double()
+    g = qa.shape[1] // ka.shape[1]
+    s_abs = max(float((qa[:, h] @ ka[:, h // g].T).max()) for h in range(qa.shape[1])) * scale
+    d = q.shape[-1]
+    return (1e-5 + 2 * np.sqrt(d) * 2.0 ** -24 * s_abs * float(v.abs().max()), 1e-5)
+
+
+@pytest.mark.parametrize("kind", ["rise", "fall", "spike"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_score_range(kind, dtype):
+    w = prefill_workload(None, None, None, hq=4, hkv=2, d=128, dtype=dtype,
+                         pages=[(300, [3, 2, 0], [100, 80, 5])], seed=5)
+    t = w.tensors
+    t["k"] = scale_keys(t["k"], kind)
+    say(f"[prefill] score range {kind} {dtype}")
+    o, lse = gpu_prefill(w)
+    ro, rl = oracle.prefill(w.desc, t["q"], t["k"], t["v"], w.scale)
+    tol = TOL[dtype] if dtype == torch.bfloat16 else fp32_score_tol(t["q"], t["k"], t["v"], w.scale)
+    e = close(o, ro, tol, f"{kind} o")
+    close(lse, rl, LSE_TOL[dtype] if dtype == torch.bfloat16 else (tol[0], 1e-5), f"{kind} lse")
+    say(f"    max_abs o={e:.3g} (atol {tol[0]:.3g})")
+
+
+@pytest.mark.parametrize("kind", ["rise", "spike"])
+def test_decode_score_range(kind):
+    w = decode_workload([1500, 7], [3, 1], [5, 0, 1200, 3],
+                        [(0, 1, 0), (0, 3, 2100), (0, 2, 70), (1, 1, 5)], hq=4, hkv=2, d=128, seed=6)
+    w.tensors["k_main"] = scale_keys(w.tensors["k_main"], kind)
+    w.tensors["k_suffix"] = scale_keys(w.tensors["k_suffix"], kind)
+    check_decode(w, tag=f"score range {kind}")
+
+
+@pytest.mark.parametrize("kind", ["rise", "spike"])
+def test_verify_score_range(kind):
+    rng = np.random.default_rng(8)
+    trees = [(0, synth.random_tree_parents(rng, 32)), (0, list(range(-1, 63))), (1, [-1, 0, 0, 1])]
+    w = verify_workload([700, 70], trees, hq=4, hkv=2, d=128, seed=9)
+    w.tensors["k_ctx"] = scale_keys(w.tensors["k_ctx"], kind)
+    w.tensors["k_tree"] = scale_keys(w.tensors["k_tree"], kind)
+    check_verify(w, tag=f"score range {kind}")

@@ -48,14 +48,14 @@ struct RowState {
 
   QFrag qf[kQSteps];
   f32x16 acc[kDB];
-  float m_used;  // running maximum of the raw scores used as the exp2 base
+  float m_used;  // exp2 base in raw-score units: a maximum of the scores so far (bf16: may lag the current one)
   float l_run;   // this lane's half of the row sum
   int koff[kBf ? kQSteps : 1];
   int voff[kBf ? 2 * kDB : 1];
   int h, n, row, ra, rb;
   uint64_t rmask;
   bool row_ok;
-  float c, tau;
+  float c, tau;  // scale * log2(e); fp32: base move threshold
 
   __device__ __forceinline__ void init_offsets(int lane) {
     if constexpr (kBf) {
@@ -136,49 +136,30 @@ struct RowState {
         }
     }
 
-    // ---- online softmax; the exp2 base moves only when a row's maximum
-    // grows by more than 2^8, so P stays <= 256 and the O rescale is rare ----
-    float mt = s[0][0];
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[bk][i]);
-    mt = pair_max(mt);
-    const bool grow = mt > m_used + tau;
-    if (__any(grow)) {
-      const float m_new = grow ? mt : m_used;
-      const float alpha = grow ? fast_exp2((m_used - m_new) * c) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int md = 0; md < kDB; ++md)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[md][i] *= alpha;
-      m_used = m_new;
-    }
-    const float mb = (m_used == -INFINITY) ? 0.f : m_used * c;
-    float ls = 0.f;
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(fmaf(s[bk][i], c, -mb));
-        s[bk][i] = e;
-        ls += e;
+    if constexpr (kBf) {
+      // ---- online softmax without a per-tile maximum: P is taken with the
+      // row's current exp2 base.  A row whose base is unset takes its
+      // maximum first; a row whose half-sum passes 2^16 (a score far above
+      // the base, or an overflow) moves its base to its maximum, and P is
+      // taken again (rare).  The base lags the true maximum by less than
+      // 2^16 in P, far inside fp32 and bf16 range. ----
+      if (__any(m_used == -INFINITY)) rebase(s, false);
+      u32x4 pw[2][2];
+      float ls = exp_pack(s, pw);
+      if (__any(pair_max(ls) > 65536.f)) {
+        rebase(s, true);
+        ls = exp_pack(s, pw);
       }
-    l_run += ls;
+      l_run += ls;
 
-    // ---- O^T += V^T P^T ----
-    int vx = voff[0];
-    if constexpr (D == 128) asm volatile("" : "+v"(vx));  // as for kx above
+      // ---- O^T += V^T P^T ----
+      int vx = voff[0];
+      if constexpr (D == 128) asm volatile("" : "+v"(vx));  // as for kx above
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-      if constexpr (kBf) {
+      for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
-          u32x4 pw;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(s[bk][8 * c2 + 2 * j], s[bk][8 * c2 + 2 * j + 1]);
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[bk][c2]);
           const unsigned char* vb = vl + (32 * bk + 16 * c2) * G::kRowBytes;
 #pragma unroll
           for (int md = 0; md < kDB; ++md) {
@@ -189,7 +170,43 @@ struct RowState {
             acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[md], 0, 0, 0);
           }
         }
-      } else {
+      sched_ld_mfma<0, 4 * kDB, 2, 8>();
+    } else {
+      // ---- fp32: online softmax; the exp2 base moves only when a row's
+      // maximum grows by more than 2^8, so P stays <= 256 and the O rescale
+      // is rare ----
+      float mt = s[0][0];
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[bk][i]);
+      mt = pair_max(mt);
+      const bool grow = mt > m_used + tau;
+      if (__any(grow)) {
+        const float m_new = grow ? mt : m_used;
+        const float alpha = grow ? fast_exp2((m_used - m_new) * c) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int md = 0; md < kDB; ++md)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[md][i] *= alpha;
+        m_used = m_new;
+      }
+      const float mb = (m_used == -INFINITY) ? 0.f : m_used * c;
+      float ls = 0.f;
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = fast_exp2(fmaf(s[bk][i], c, -mb));
+          s[bk][i] = e;
+          ls += e;
+        }
+      l_run += ls;
+
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 32 * bk + reg_key(i, h);
@@ -199,9 +216,46 @@ struct RowState {
             acc[md] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[bk][i], acc[md], 0, 0, 0);
           }
         }
-      }
     }
-    if constexpr (kBf) sched_ld_mfma<0, 4 * kDB, 2, 8>();
+  }
+
+  // bf16: move each row's base to its maximum so far -- only rows that have
+  // none yet, or with `all` every row whose maximum grew; O and l scale by
+  // the change.
+  __device__ __forceinline__ void rebase(const f32x16 (&s)[2], bool all) {
+    float mt = s[0][0];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[bk][i]);
+    mt = pair_max(mt);
+    const bool grow = (all || m_used == -INFINITY) && mt > m_used;
+    const float m_new = grow ? mt : m_used;
+    const float alpha = (grow && m_used != -INFINITY) ? fast_exp2((m_used - m_new) * c) : 1.f;
+    l_run *= alpha;
+#pragma unroll
+    for (int md = 0; md < kDB; ++md)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[md][i] *= alpha;
+    m_used = m_new;
+  }
+
+  // bf16: P = exp2(c s - c m) as bf16 pairs, the P^T operands of the PV
+  // MFMAs (pw[bk][c2]: keys 16 c2.. of 32-key block bk); returns the lane's
+  // part of the row sum.
+  __device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], u32x4 (&pw)[2][2]) const {
+    const float mb = (m_used == -INFINITY) ? 0.f : m_used * c;
+    float ls = 0.f;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float e0 = fast_exp2(fmaf(s[bk][2 * j], c, -mb));
+        const float e1 = fast_exp2(fmaf(s[bk][2 * j + 1], c, -mb));
+        ls += e0 + e1;
+        pw[bk][j >> 2][j & 3] = pack_bf16x2(e0, e1);
+      }
+    return ls;
   }
 
   // Byte offset of the transposing V read (r, md) of this lane.  At
