@@ -12,13 +12,14 @@
 //                     S^T = K Q^T and dP^T = V dO^T per 64-key tile and adds
 //                     K^T dS^T into dQ^T held in registers
 //   bwd_dkdv_kernel   key-major, over the plan's key tiles: each wave holds
-//                     32 keys of one KV head and walks the 64-row tiles (and
+//                     16 keys of one KV head and walks the 64-row tiles (and
 //                     every query head of the group) that can see them,
 //                     adding dO^T P into dV^T and Q^T dS into dK^T
-// Both main kernels use the forward's MFMA formulations: an operand read
-// from an LDS tile in permuted row order against one held in registers
-// (v_mfma_f32_32x32x16_bf16), and a transposing LDS read (ds_read_b64_tr_b16)
-// against a product taken straight from accumulators.  No atomics: each
+// Both main kernels pair an operand read from an LDS tile against one held
+// in registers, and a transposing LDS read (ds_read_b64_tr_b16) against a
+// product taken straight from accumulators: 32x32x16 bf16 MFMAs in the
+// query-major kernel (the forward's formulation), 16x16x32 in the key-major
+// one (half the registers per wave, so two waves share a SIMD).  No atomics: each
 // output element is written by exactly one wave, so results are
 // deterministic.
 #include "ta_device.h"
@@ -219,16 +220,24 @@ struct RowMeta {
   int32_t ra[64], rb[64];
 };
 
-// Two waves of 32 keys (one 64-key tile of one KV head) per workgroup; one
-// wave per SIMD, so the two accumulators dK^T, dV^T and the key's K and V
-// operands stay in registers.
+// Four waves of 16 keys (one 64-key tile of one KV head) per workgroup, two
+// waves per SIMD.  Per wave, with 16x16x32 MFMAs (A: lane l holds row l % 16,
+// k in [8 (l / 16), +8); B: column l % 16, same k; D: column l % 16, rows
+// 4 (l / 16) .. +3):
+//   S = Q K^T and dP = dO V^T per 16-row block (Q, dO rows from LDS; K, V
+//     of the wave's keys in registers): lane l holds key l % 16 and rows
+//     4 (l / 16) + i of the block;
+//   dV^T += dO^T P and dK^T += Q^T dS per 32 rows: the A operand is a pair
+//     of transposing LDS reads (rows 4 (l / 16) .. +3 of each 16-row block at
+//     16 consecutive d), the B operand the lane's own P / dS values of those
+//     two blocks, packed in the same row order.
 template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   using T = __bf16;
   using G = TileGeom<T, D>;
-  constexpr int NW = 2;
-  constexpr int kQSteps = D / 16;
-  constexpr int kDB = D / 32;
+  constexpr int NW = 4;
+  constexpr int kKS = D / 32;  // k-steps of 32 over head_dim
+  constexpr int kDB = D / 16;  // 16-wide blocks of head_dim
   constexpr int kStage = G::kStageBytes + int(sizeof(RowMeta));
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[kStage];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[kStage];
@@ -286,42 +295,39 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     *reinterpret_cast<int4*>(&m->rb[x]) = d;
   };
 
-  // this wave's 32 keys as B operands (lane: key n, dims (D/2) h + 8 st ..)
-  const int h = lane >> 5, n = lane & 31;
-  const int key = wi.row0 + 32 * wave + n;
-  const bool key_ok = 32 * wave + n < wi.nrows;
-  bf16x8 kf[kQSteps], vf[kQSteps];
+  // this wave's 16 keys as B operands (lane: key l % 16, dims 32 ks + 8 g ..)
+  const int g = lane >> 4, n16 = lane & 15;
+  const int key = wi.row0 + 16 * wave + n16;
+  const bool key_ok = 16 * wave + n16 < wi.nrows;
+  bf16x8 kf[kKS], vf[kKS];
   {
-    const T* krow = reinterpret_cast<const T*>(p.k) + (int64_t(key) * p.hkv + kvh) * D + (D / 2) * h;
-    const T* vrow = reinterpret_cast<const T*>(p.v) + (int64_t(key) * p.hkv + kvh) * D + (D / 2) * h;
+    const T* krow = reinterpret_cast<const T*>(p.k) + (int64_t(key) * p.hkv + kvh) * D + 8 * g;
+    const T* vrow = reinterpret_cast<const T*>(p.v) + (int64_t(key) * p.hkv + kvh) * D + 8 * g;
 #pragma unroll
-    for (int s = 0; s < kQSteps; ++s) {
+    for (int ks = 0; ks < kKS; ++ks) {
       u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
       if (key_ok) {
-        a = *reinterpret_cast<const u32x4*>(krow + 8 * s);
-        b = *reinterpret_cast<const u32x4*>(vrow + 8 * s);
+        a = *reinterpret_cast<const u32x4*>(krow + 32 * ks);
+        b = *reinterpret_cast<const u32x4*>(vrow + 32 * ks);
       }
-      kf[s] = __builtin_bit_cast(bf16x8, a);
-      vf[s] = __builtin_bit_cast(bf16x8, b);
+      kf[ks] = __builtin_bit_cast(bf16x8, a);
+      vf[ks] = __builtin_bit_cast(bf16x8, b);
     }
   }
-  const int qx = G::at(key_perm(n), D * h);  // permuted-row operand reads of Q and dO
-  int toff[2 * kDB];                          // transposing reads of dO and Q
-  {
-    const int m16 = lane & 15, grp = lane >> 4;
+  // LDS offsets.  Q / dO row n16 of a 16-row block at dims 32 ks + 8 g: the
+  // k-steps differ only in swizzled chunk bits (qx ^ 64 ks), the blocks by
+  // whole 16-row steps.  Transposing reads: lane m of a 16-lane group
+  // addresses row 4 g + m / 4 at dims 16 db + 4 (m % 4); the d-blocks differ
+  // in chunk bits (tx ^ 32 db).
+  const int qx = G::at(n16, 16 * g);
+  const int tx = G::at(4 * g + (n16 >> 2), 8 * (n16 & 3));
+  f32x4 dk[kDB], dv[kDB];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+  for (int db = 0; db < kDB; ++db)
 #pragma unroll
-      for (int md = 0; md < kDB; ++md)
-        toff[r * kDB + md] = G::at(8 * (grp >> 1) + 4 * r + (m16 >> 2), 2 * (32 * md + 16 * (grp & 1) + 4 * (m16 & 3)));
-  }
-  f32x16 dk[kDB], dv[kDB];
-#pragma unroll
-  for (int md = 0; md < kDB; ++md)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk[md][i] = 0.f;
-      dv[md][i] = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      dk[db][i] = 0.f;
+      dv[db][i] = 0.f;
     }
 
   auto consume = [&](const unsigned char* stage, int s) {
@@ -334,77 +340,66 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // (rows past the segment end hold zero Q, dO, lse2 and Dd: they add 0)
     const bool masked = r0 < (r < n_a ? wi.a_full : wi.out);
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
-      // S = Q K^T and dP = dO V^T for rows [32 b2, 32 b2 + 32) of the tile:
-      // lane (key n, h) holds rows 32 b2 + reg_key(i, h)
-      f32x16 sc = {}, dp = {};
+    for (int h2 = 0; h2 < 2; ++h2) {
+      u32x4 pp, pd;
 #pragma unroll
-      for (int st = 0; st < kQSteps; ++st) {
-        const int off = (qx ^ (16 * st)) + 32 * b2 * G::kRowBytes;
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qt + off), kf[st], sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(gt + off), vf[st], dp, 0, 0, 0);
-      }
-      sched_ld_mfma<0, 2 * kQSteps, 1, 4>();
-      // the lane's 16 rows are 32 b2 + reg_key(i, h): four runs of 4
-      // consecutive rows, read as float4 / int4
-      float l2v[16], ddv[16];
+      for (int b1 = 0; b1 < 2; ++b1) {
+        const int rb = 2 * h2 + b1;
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int lr = 32 * b2 + reg_key(4 * q4, h);
-        const float4 a = *reinterpret_cast<const float4*>(&m->l2[lr]);
-        const float4 d = *reinterpret_cast<const float4*>(&m->dd[lr]);
-        l2v[4 * q4] = a.x; l2v[4 * q4 + 1] = a.y; l2v[4 * q4 + 2] = a.z; l2v[4 * q4 + 3] = a.w;
-        ddv[4 * q4] = d.x; ddv[4 * q4 + 1] = d.y; ddv[4 * q4 + 2] = d.z; ddv[4 * q4 + 3] = d.w;
-      }
-      bool vis[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) vis[i] = true;
-      if (masked) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int lr = 32 * b2 + reg_key(4 * q4, h);
+        for (int ks = 0; ks < kKS; ++ks) {
+          const int off = (qx ^ (64 * ks)) + 16 * rb * G::kRowBytes;
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(qt + off), kf[ks], sc, 0, 0,
+                                                        0);
+          dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(gt + off), vf[ks], dp, 0, 0,
+                                                        0);
+        }
+        // the lane's rows 16 rb + 4 g + i: one float4 / int4 of each row value
+        const int lr = 16 * rb + 4 * g;
+        const float4 l2 = *reinterpret_cast<const float4*>(&m->l2[lr]);
+        const float4 dd = *reinterpret_cast<const float4*>(&m->dd[lr]);
+        const float l2v[4] = {l2.x, l2.y, l2.z, l2.w}, ddv[4] = {dd.x, dd.y, dd.z, dd.w};
+        bool vis[4] = {true, true, true, true};
+        if (masked) {
           const int4 ra4 = *reinterpret_cast<const int4*>(&m->ra[lr]);
           const int4 rb4 = *reinterpret_cast<const int4*>(&m->rb[lr]);
-          const int ra[4] = {ra4.x, ra4.y, ra4.z, ra4.w}, rb[4] = {rb4.x, rb4.y, rb4.z, rb4.w};
+          const int ra[4] = {ra4.x, ra4.y, ra4.z, ra4.w}, rbv[4] = {rb4.x, rb4.y, rb4.z, rb4.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = r0 + lr + e;
-            vis[4 * q4 + e] = (row < rhi) & (branch_keys ? ((key >= rb[e]) & (key <= row)) : (key < ra[e]));
+          for (int i = 0; i < 4; ++i) {
+            const int row = r0 + lr + i;
+            vis[i] = (row < rhi) & (branch_keys ? ((key >= rbv[i]) & (key <= row)) : (key < ra[i]));
           }
         }
-      }
-      u32x4 pp[2], pd[2];
+        float pr[4], ds[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float pr[2], ds[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int i = 2 * j + e;
-          pr[e] = vis[i] ? fast_exp2(fmaf(sc[i], p.c, -l2v[i])) : 0.f;
-          ds[e] = pr[e] * (dp[i] - ddv[i]);
+        for (int i = 0; i < 4; ++i) {
+          pr[i] = vis[i] ? fast_exp2(fmaf(sc[i], p.c, -l2v[i])) : 0.f;
+          ds[i] = pr[i] * (dp[i] - ddv[i]);
         }
-        pp[j >> 2][j & 3] = pack_bf16x2(pr[0], pr[1]);
-        pd[j >> 2][j & 3] = pack_bf16x2(ds[0], ds[1]);
+        pp[2 * b1] = pack_bf16x2(pr[0], pr[1]);
+        pp[2 * b1 + 1] = pack_bf16x2(pr[2], pr[3]);
+        pd[2 * b1] = pack_bf16x2(ds[0], ds[1]);
+        pd[2 * b1 + 1] = pack_bf16x2(ds[2], ds[3]);
       }
+      sched_ld_mfma<0, 4 * kKS, 1, 4>();
       // dV^T += dO^T P and dK^T += Q^T dS over these 32 rows
+      const bf16x8 bp = __builtin_bit_cast(bf16x8, pp);
+      const bf16x8 bd = __builtin_bit_cast(bf16x8, pd);
+      const int rowb = 32 * h2 * G::kRowBytes;
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16x8 bp = __builtin_bit_cast(bf16x8, pp[c2]);
-        const bf16x8 bd = __builtin_bit_cast(bf16x8, pd[c2]);
-        const int rowb = (32 * b2 + 16 * c2) * G::kRowBytes;
-#pragma unroll
-        for (int md = 0; md < kDB; ++md) {
-          const s16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(gt + rowb + toff[md]));
-          const s16x4 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(gt + rowb + toff[kDB + md]));
-          const s16x4 gg[2] = {g0, g1};
-          dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, gg), bp, dv[md], 0, 0, 0);
-          const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(qt + rowb + toff[md]));
-          const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(qt + rowb + toff[kDB + md]));
-          const s16x4 qq[2] = {q0, q1};
-          dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qq), bd, dk[md], 0, 0, 0);
-        }
+      for (int db = 0; db < kDB; ++db) {
+        const int o0 = (tx ^ (32 * db)) + rowb;
+        const int o1 = o0 + 16 * G::kRowBytes;
+        const s16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(gt + o0));
+        const s16x4 g1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(gt + o1));
+        const s16x4 gg[2] = {g0, g1};
+        dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, gg), bp, dv[db], 0, 0, 0);
+        const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(qt + o0));
+        const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(qt + o1));
+        const s16x4 qq[2] = {q0, q1};
+        dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qq), bd, dk[db], 0, 0, 0);
       }
-      sched_ld_mfma<0, 4 * kDB, 2, 8>();
+      sched_ld_mfma<0, 2 * kDB, 2, 8>();
     }
   };
 
@@ -438,16 +433,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   T* kd = reinterpret_cast<T*>(p.dk) + (int64_t(key) * p.hkv + kvh) * D;
   T* vd = reinterpret_cast<T*>(p.dv) + (int64_t(key) * p.hkv + kvh) * D;
 #pragma unroll
-  for (int md = 0; md < kDB; ++md)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = 32 * md + 8 * g + 4 * h;
-      u32x2 a = {pack_bf16x2(dk[md][4 * g] * p.scale, dk[md][4 * g + 1] * p.scale),
-                 pack_bf16x2(dk[md][4 * g + 2] * p.scale, dk[md][4 * g + 3] * p.scale)};
-      u32x2 b = {pack_bf16x2(dv[md][4 * g], dv[md][4 * g + 1]), pack_bf16x2(dv[md][4 * g + 2], dv[md][4 * g + 3])};
-      *reinterpret_cast<u32x2*>(kd + d0) = a;
-      *reinterpret_cast<u32x2*>(vd + d0) = b;
-    }
+  for (int db = 0; db < kDB; ++db) {
+    const int d0 = 16 * db + 4 * g;
+    u32x2 a = {pack_bf16x2(dk[db][0] * p.scale, dk[db][1] * p.scale),
+               pack_bf16x2(dk[db][2] * p.scale, dk[db][3] * p.scale)};
+    u32x2 b = {pack_bf16x2(dv[db][0], dv[db][1]), pack_bf16x2(dv[db][2], dv[db][3])};
+    *reinterpret_cast<u32x2*>(kd + d0) = a;
+    *reinterpret_cast<u32x2*>(vd + d0) = b;
+  }
 }
 
 template __global__ void bwd_prep_kernel<32>(BwdParams);
@@ -474,7 +467,7 @@ static hipError_t launch_bwd_d(const BwdParams& p, int n_work, int n_kwork, hipS
                          dim3(256), 0, st, p);
   }
   if (n_kwork > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(unsigned(n_kwork) * unsigned(p.hkv)), dim3(128), 0, st, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(unsigned(n_kwork) * unsigned(p.hkv)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
