@@ -73,10 +73,12 @@ extern "C" {
 #define TA_FIELD_DECODE_ROWS 6  /* decode:  [rows][5] main_start, main_len, suffix_start, visible suffix length, position */
 #define TA_FIELD_VERIFY_MASK 7  /* verify:  [nodes] ancestor bitmask (bit j: node j of the same branch is an ancestor or itself) */
 #define TA_FIELD_VERIFY_ROWS 8  /* verify:  [nodes][4] ctx_start, ctx_len, tree_base (abs node 0 of the branch), position */
-#define TA_FIELD_BWD_WORK 10    /* prefill: [items][10] key-major backward items: key0, n_keys, a_lo, a_full, a_hi,
-                                   b_lo, b_hi, b_full, flags (2: branch-area keys), row tiles walked; rows
+#define TA_FIELD_BWD_WORK 10    /* prefill: [items][12] key-major backward items: key0, n_keys, a_lo, a_full, a_hi,
+                                   b_lo, b_hi, b_full, flags (2: branch-area keys), tile_lo, tile_hi, slot; rows
                                    [a_lo, a_hi) and [b_lo, b_hi) can see the keys, rows from a_full / b_full on
-                                   see all of them */
+                                   see all of them; the item walks row tiles [tile_lo, tile_hi) of those
+                                   segments (A's, then B's); a key tile whose walk is long is split into such
+                                   pieces, each writing fp32 partials to its slot (-1: not split) */
 #define TA_FIELD_PAGED_TILES 11 /* paged: [tiles of A, then tiles of B] cache row of the first token of each
                                    64-token tile, by virtual position / 64 (A: main streams or contexts; B: decode
                                    suffixes, absent for verify) */
@@ -311,7 +313,10 @@ int tree_attn_prefill(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hk
                       size_t scratch_bytes, void* stream);
 
 /* Scratch bytes tree_attn_prefill_backward needs: two fp32 values per
- * (query head, row) (the row sums Dd = sum_d dO * O and lse * log2 e). */
+ * (query head, row) (the row sums Dd = sum_d dO * O and lse * log2 e), plus
+ * fp32 partial dK and dV of the key tiles whose walk the plan splits
+ * (2 x 64 x head_dim per KV head and piece; sized here for Hkv = hq and
+ * head_dim = 128, an upper bound of what any call with this hq uses). */
 int tree_attn_backward_scratch_bytes(const ta_plan* plan, int32_t hq, size_t* bytes);
 
 /* Backward of tree_attn_prefill: the gradients of o with respect to q, k and

@@ -46,17 +46,40 @@ def check_prefill_plan(desc):
 
 
 def check_backward_items(desc, plan):
-    """Key-major items of the backward: every key lies in exactly one item,
-    inside one page region (main stream or branch area), and every row that
-    can see a key lies in one of its item's row segments."""
+    """Key-major items of the backward: every key lies in exactly one key
+    tile, inside one page region (main stream or branch area), and every row
+    that can see a key lies in one of its tile's row segments.  A tile whose
+    walk is long comes as pieces with the same segments whose row-tile ranges
+    partition the walk, each with its own partial slot (slots of a tile are
+    consecutive); an unsplit tile has slot -1."""
     items = plan.export("bwd_work")
     T = desc.total_tokens()
+    tiles = {}
+    for w in items:
+        tiles.setdefault((int(w[0]), int(w[1])), []).append(w)
     owner = np.full(T, -1, np.int64)
-    for n, w in enumerate(items):
-        k0, nk = int(w[0]), int(w[1])
+    first = {}
+    slots = []
+    for n, ((k0, nk), pieces) in enumerate(sorted(tiles.items())):
         assert 0 < nk <= 64
         assert (owner[k0:k0 + nk] == -1).all()
         owner[k0:k0 + nk] = n
+        w0 = pieces[0]
+        for w in pieces:
+            assert np.array_equal(w[:9], w0[:9])
+        n_rt = -(-(int(w0[4]) - int(w0[2])) // 64) + -(-(int(w0[6]) - int(w0[5])) // 64)
+        pieces = sorted(pieces, key=lambda w: int(w[9]))
+        assert [int(w[9]) for w in pieces] == [0] + [int(w[10]) for w in pieces[:-1]]
+        assert int(pieces[-1][10]) == n_rt
+        assert all(int(w[10]) - int(w[9]) <= 100 for w in pieces)
+        if len(pieces) == 1:
+            assert int(pieces[0][11]) == -1
+        else:
+            sl = [int(w[11]) for w in pieces]
+            assert sl == list(range(sl[0], sl[0] + len(sl)))
+            slots += sl
+        first[n] = w0
+    assert sorted(slots) == list(range(len(slots)))
     assert (owner >= 0).all()
     base = 0
     for p, sl in desc.page_slices():
@@ -66,7 +89,7 @@ def check_backward_items(desc, plan):
         mask = oracle.ancestor_mask_page(P, L, C)
         keys = range(t) if t <= 2048 else range(0, t, 37)  # every key of small pages, a sample of large ones
         for j in keys:
-            w = items[owner[base + j]]
+            w = first[owner[base + j]]
             k0, nk, flags = int(w[0]), int(w[1]), int(w[8])
             in_branch = base + j >= base + M
             assert bool(flags & 2) == in_branch
@@ -78,6 +101,16 @@ def check_backward_items(desc, plan):
             full = np.r_[np.arange(w[3], w[4]), np.arange(w[7], w[6])]
             assert mask[full - base, j].all(), (p, j)
         base += t
+
+
+def test_backward_long_walks_are_split():
+    """The one-page workload's early main-stream key tiles are seen by more
+    than 100 row tiles: their walks come as pieces with partial slots."""
+    plan = ta.plan_for(synth.config2(with_tensors=False).desc)
+    items = plan.export("bwd_work")
+    split = items[items[:, 11] >= 0]
+    assert len(split) > 0 and (split[:, 10] - split[:, 9] <= 100).all()
+    assert ta.backward_scratch_bytes(plan, 16) >= 2 * 16 * 8772 * 4 + len(split) * 16 * 2 * 64 * 128 * 4
 
 
 def test_prefill_plan_configs_exact():

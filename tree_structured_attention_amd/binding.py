@@ -52,7 +52,7 @@ FIELD = {
     "bwd_work": 10,
     "paged_tiles": 11,
 }
-FIELD_WIDTH = {"pages": 5, "branches": 3, "decode_rows": 5, "verify_rows": 4, "work": 11, "bwd_work": 10}
+FIELD_WIDTH = {"pages": 5, "branches": 3, "decode_rows": 5, "verify_rows": 4, "work": 11, "bwd_work": 12}
 
 
 class TreeAttnError(RuntimeError):

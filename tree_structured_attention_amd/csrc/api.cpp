@@ -158,7 +158,7 @@ extern "C" int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t
       if (k != TA_PLAN_PREFILL) break;
       for (const WorkItem& w : plan->kwork)
         work_tmp.insert(work_tmp.end(), {w.row0, w.nrows, w.a_lo, w.a_full, w.a_hi, w.b_lo, w.b_hi, w.out,
-                                         w.flags, w.tile_hi});
+                                         w.flags, w.tile_lo, w.tile_hi, w.b_full});
       src = &work_tmp;
       break;
     case TA_FIELD_PAGED_TILES:
@@ -310,10 +310,20 @@ extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, 
   return hip_status(launch_merge_for(plan, dtype, p, head_dim, st), "decode merge launch");
 }
 
+namespace {
+
+// fp32 partial dK, dV of the split key tiles: [slots, hkv, 2, 64 keys, d]
+int64_t kpart_bytes(const ta_plan* plan, int64_t hkv, int64_t head_dim) {
+  return plan->n_kpart * hkv * 2 * kKeyTile * head_dim * 4;
+}
+
+}  // namespace
+
 extern "C" int tree_attn_backward_scratch_bytes(const ta_plan* plan, int32_t hq, size_t* bytes) {
   if (!plan || !bytes) return fail(TA_ERR_INVALID_ARG, "backward_scratch_bytes: NULL argument");
   if (hq <= 0) return fail(TA_ERR_INVALID_ARG, "backward_scratch_bytes: hq must be positive");
-  *bytes = size_t(2 * align256(plan->n_rows * hq * 4));
+  // the partials are sized for the largest call: Hkv <= Hq, head_dim <= 128
+  *bytes = size_t(2 * align256(plan->n_rows * hq * 4) + kpart_bytes(plan, hq, 128));
   return TA_OK;
 }
 
@@ -337,7 +347,7 @@ extern "C" int tree_attn_prefill_backward(const ta_plan* plan, int32_t dtype, in
   if (rows > 0) {
     if (!scratch) return fail(TA_ERR_WORKSPACE, "prefill_backward: scratch is NULL");
     if (!aligned(scratch, 256)) return fail(TA_ERR_INVALID_ARG, "prefill_backward: scratch must be 256-byte aligned");
-    if (int64_t(scratch_bytes) < 2 * half)
+    if (int64_t(scratch_bytes) < 2 * half + kpart_bytes(plan, hkv, head_dim))
       return fail(TA_ERR_WORKSPACE, "prefill_backward: scratch smaller than tree_attn_backward_scratch_bytes");
   }
   if ((rc = check_uploaded(plan, "prefill_backward"))) return rc;
@@ -357,6 +367,8 @@ extern "C" int tree_attn_prefill_backward(const ta_plan* plan, int32_t dtype, in
   p.dd = reinterpret_cast<float*>(static_cast<unsigned char*>(scratch) + half);
   p.work = reinterpret_cast<const WorkItem*>(dev + plan->layout.work);
   p.kwork = reinterpret_cast<const WorkItem*>(dev + plan->layout.kwork);
+  p.kmerge = reinterpret_cast<const KMerge*>(dev + plan->layout.kmerge);
+  p.kpart = reinterpret_cast<float*>(static_cast<unsigned char*>(scratch) + 2 * half);
   p.row_a = reinterpret_cast<const int32_t*>(dev + plan->layout.row_a);
   p.row_b = reinterpret_cast<const int32_t*>(dev + plan->layout.row_b);
   p.hq = hq;
@@ -365,8 +377,8 @@ extern "C" int tree_attn_prefill_backward(const ta_plan* plan, int32_t dtype, in
   p.c = scale * 1.4426950408889634f;
   p.scale = scale;
   p.n_rows = rows;
-  return hip_status(launch_backward(p, int(plan->work.size()), int(plan->kwork.size()), head_dim,
-                                    static_cast<hipStream_t>(stream)),
+  return hip_status(launch_backward(p, int(plan->work.size()), int(plan->kwork.size()), int(plan->kmerge.size()),
+                                    head_dim, static_cast<hipStream_t>(stream)),
                     "prefill_backward launch");
 }
 

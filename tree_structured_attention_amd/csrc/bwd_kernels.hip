@@ -6,7 +6,7 @@
 //   P = exp(scale q k^T - lse)   (lse saved by the forward)
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Dd),  Dd = rowsum(dO * O)
 //   dQ = scale dS K,  dK = scale dS^T Q
-// Three launches:
+// Launches:
 //   bwd_prep_kernel   Dd and lse * log2(e) per (query head, row), fp32
 //   bwd_dq_kernel     query-major, over the forward's row tiles: recomputes
 //                     S^T = K Q^T and dP^T = V dO^T per 64-key tile and adds
@@ -14,7 +14,9 @@
 //   bwd_dkdv_kernel   key-major, over the plan's key tiles: each wave holds
 //                     16 keys of one KV head and walks the 64-row tiles (and
 //                     every query head of the group) that can see them,
-//                     adding dO^T P into dV^T and Q^T dS into dK^T
+//                     adding dO^T P into dV^T and Q^T dS into dK^T; a long
+//                     walk comes as pieces that write fp32 partials
+//   bwd_kmerge_kernel the partials of each split key tile summed in order
 // Both main kernels pair an operand read from an LDS tile against one held
 // in registers, and a transposing LDS read (ds_read_b64_tr_b16) against a
 // product taken straight from accumulators: 32x32x16 bf16 MFMAs in the
@@ -248,25 +250,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   const WorkItem wi = p.kwork[blockIdx.x / unsigned(p.hkv)];
   const bool branch_keys = (wi.flags & kKeyBranch) != 0;
   const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
-  const int n_rt = n_a + (wi.b_hi - wi.b_lo + kKeyTile - 1) / kKeyTile;  // row tiles per query head
-  const int n_steps = n_rt * p.group;                                      // (head, row tile) pairs
+  const int n_pc = wi.tile_hi - wi.tile_lo;  // this piece's row tiles per query head
+  const int n_steps = n_pc * p.group;        // (head, row tile) pairs
   const int64_t q_stride = int64_t(p.hq) * D * 2;
   auto rt0 = [&](int r) { return r < n_a ? wi.a_lo + r * kKeyTile : wi.b_lo + (r - n_a) * kKeyTile; };
   auto rt_hi = [&](int r) { return r < n_a ? wi.a_hi : wi.b_hi; };
 
   TileLoader<T, D, NW> loader;
   loader.init(lane, wave, q_stride);
-  // step s = (query head j of the group, row tile r): Q and dO tiles go to
-  // the stage by DMA; the row values by wave 0, through registers
+  // step s = (query head j of the group, row tile r of the piece): Q and dO
+  // tiles go to the stage by DMA; the row values by wave 0, through registers
   auto issue = [&](int s, unsigned char* stage) {
-    const int j = s / n_rt, r = s % n_rt;
+    const int j = s / n_pc, r = wi.tile_lo + s % n_pc;
     const int head = kvh * p.group + j;
     const unsigned char* qb = reinterpret_cast<const unsigned char*>(p.q) + int64_t(head) * D * 2;
     const unsigned char* gb = reinterpret_cast<const unsigned char*>(p.dO) + int64_t(head) * D * 2;
     loader.issue(stage, qb, gb, rt0(r), rt_hi(r), q_stride, wave);
   };
   auto load_meta = [&](int s, float4& a, float4& b, int4& c, int4& d) {
-    const int j = s / n_rt, r = s % n_rt;
+    const int j = s / n_pc, r = wi.tile_lo + s % n_pc;
     const int head = kvh * p.group + j;
     const int r0 = rt0(r), rhi = min(rt_hi(r), r0 + kKeyTile);
     const int x = r0 + 4 * (lane & 15);
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     const unsigned char* qt = stage;
     const unsigned char* gt = stage + G::kTileBytes;
     const RowMeta* m = reinterpret_cast<const RowMeta*>(stage + G::kStageBytes);
-    const int r = s % n_rt;
+    const int r = wi.tile_lo + s % n_pc;
     const int r0 = rt0(r), rhi = rt_hi(r);
     // row tiles past the segment's first fully visible row need no test
     // (rows past the segment end hold zero Q, dO, lse2 and Dd: they add 0)
@@ -430,6 +432,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   }
 
   if (!key_ok) return;
+  if (wi.b_full >= 0) {
+    // a piece of a split key tile: fp32 partials, summed by bwd_kmerge_kernel
+    float* kp = p.kpart + (int64_t(wi.b_full) * p.hkv + kvh) * 2 * kKeyTile * D + (16 * wave + n16) * D;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      *reinterpret_cast<f32x4*>(kp + 16 * db + 4 * g) = dk[db];
+      *reinterpret_cast<f32x4*>(kp + kKeyTile * D + 16 * db + 4 * g) = dv[db];
+    }
+    return;
+  }
   T* kd = reinterpret_cast<T*>(p.dk) + (int64_t(key) * p.hkv + kvh) * D;
   T* vd = reinterpret_cast<T*>(p.dv) + (int64_t(key) * p.hkv + kvh) * D;
 #pragma unroll
@@ -443,20 +455,47 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// Split key tiles: dK, dV of keys [key0, key0 + nkeys) of one KV head per
+// workgroup, the sum of the pieces' fp32 partials in slot order (fixed, so
+// results are deterministic).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_kmerge_kernel(BwdParams p) {
+  const int kvh = int(blockIdx.x % unsigned(p.hkv));
+  const KMerge km = p.kmerge[blockIdx.x / unsigned(p.hkv)];
+  const int n4 = km.nkeys * D / 4;
+  for (int e4 = threadIdx.x; e4 < n4; e4 += 256) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    for (int c = 0; c < km.count; ++c) {
+      const float4* src =
+          reinterpret_cast<const float4*>(p.kpart + (int64_t(km.first + c) * p.hkv + kvh) * 2 * kKeyTile * D);
+      const float4 x = src[e4], y = src[kKeyTile * D / 4 + e4];
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+    }
+    const int key = km.key0 + (4 * e4) / D, d = (4 * e4) % D;
+    const int64_t at = (int64_t(key) * p.hkv + kvh) * D + d;
+    *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(p.dk) + at) =
+        u32x2{pack_bf16x2(a.x * p.scale, a.y * p.scale), pack_bf16x2(a.z * p.scale, a.w * p.scale)};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(p.dv) + at) =
+        u32x2{pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
+  }
+}
+
 template __global__ void bwd_prep_kernel<32>(BwdParams);
 template __global__ void bwd_prep_kernel<64>(BwdParams);
 template __global__ void bwd_prep_kernel<128>(BwdParams);
 #define TA_INSTANTIATE_BWD(D)                              \
   template __global__ void bwd_dq_kernel<D, 1>(BwdParams); \
   template __global__ void bwd_dq_kernel<D, 2>(BwdParams); \
-  template __global__ void bwd_dkdv_kernel<D>(BwdParams);
+  template __global__ void bwd_dkdv_kernel<D>(BwdParams); \
+  template __global__ void bwd_kmerge_kernel<D>(BwdParams);
 TA_INSTANTIATE_BWD(32)
 TA_INSTANTIATE_BWD(64)
 TA_INSTANTIATE_BWD(128)
 #undef TA_INSTANTIATE_BWD
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdParams& p, int n_work, int n_kwork, hipStream_t st) {
+static hipError_t launch_bwd_d(const BwdParams& p, int n_work, int n_kwork, int n_kmerge, hipStream_t st) {
   const int64_t pairs = p.n_rows * p.hq;
   if (pairs > 0) hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(unsigned((pairs + 3) / 4)), dim3(256), 0, st, p);
   if (n_work > 0) {
@@ -468,13 +507,15 @@ static hipError_t launch_bwd_d(const BwdParams& p, int n_work, int n_kwork, hipS
   }
   if (n_kwork > 0)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(unsigned(n_kwork) * unsigned(p.hkv)), dim3(256), 0, st, p);
+  if (n_kmerge > 0)
+    hipLaunchKernelGGL((bwd_kmerge_kernel<D>), dim3(unsigned(n_kmerge) * unsigned(p.hkv)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_backward(const BwdParams& p, int n_work, int n_kwork, int d, hipStream_t st) {
-  if (d == 32) return launch_bwd_d<32>(p, n_work, n_kwork, st);
-  if (d == 64) return launch_bwd_d<64>(p, n_work, n_kwork, st);
-  if (d == 128) return launch_bwd_d<128>(p, n_work, n_kwork, st);
+hipError_t launch_backward(const BwdParams& p, int n_work, int n_kwork, int n_kmerge, int d, hipStream_t st) {
+  if (d == 32) return launch_bwd_d<32>(p, n_work, n_kwork, n_kmerge, st);
+  if (d == 64) return launch_bwd_d<64>(p, n_work, n_kwork, n_kmerge, st);
+  if (d == 128) return launch_bwd_d<128>(p, n_work, n_kwork, n_kmerge, st);
   return hipErrorInvalidValue;
 }
 

@@ -118,6 +118,8 @@ void pack_blob(ta_plan* p) {
   off = align256(off + int64_t(p->merge.size() * sizeof(MergeRow)));
   L.kwork = off;
   off = align256(off + int64_t(p->kwork.size() * sizeof(WorkItem)));
+  L.kmerge = off;
+  off = align256(off + int64_t(p->kmerge.size() * sizeof(KMerge)));
   L.trees = off;
   off = align256(off + int64_t(p->tree_tab.size() * 4));
   L.tile_a = off;
@@ -136,6 +138,7 @@ void pack_blob(ta_plan* p) {
   put(L.mask, p->row_mask.data(), p->row_mask.size() * 8);
   put(L.merge, p->merge.data(), p->merge.size() * sizeof(MergeRow));
   put(L.kwork, p->kwork.data(), p->kwork.size() * sizeof(WorkItem));
+  put(L.kmerge, p->kmerge.data(), p->kmerge.size() * sizeof(KMerge));
   put(L.trees, p->tree_tab.data(), p->tree_tab.size() * 4);
   put(L.tile_a, p->tile_a.data(), p->tile_a.size() * 4);
   put(L.tile_b, p->tile_b.data(), p->tile_b.size() * 4);
@@ -258,6 +261,18 @@ extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* 
       }
     }
     auto row_tiles = [](int64_t lo, int64_t hi) { return hi > lo ? (hi - lo + kKeyTile - 1) / kKeyTile : 0; };
+    // one item per key tile, or near-equal pieces of its row tiles when the
+    // walk is long (they write fp32 partials that a merge sums in order)
+    auto push_key_item = [&](WorkItem w, int64_t n_rt) {
+      const int64_t np = std::max<int64_t>(1, (n_rt + kBwdMaxRowTiles - 1) / kBwdMaxRowTiles);
+      if (np > 1) pl->kmerge.push_back(KMerge{w.row0, w.nrows, int32_t(pl->n_kpart), int32_t(np)});
+      for (int64_t i = 0; i < np; ++i) {
+        w.tile_lo = int32_t(n_rt * i / np);
+        w.tile_hi = int32_t(n_rt * (i + 1) / np);
+        w.b_full = np > 1 ? int32_t(pl->n_kpart++) : -1;
+        pl->kwork.push_back(w);
+      }
+    };
     for (int64_t k0 = base; k0 < base + M; k0 += kKeyTile) {
       const int64_t k1 = std::min(base + M, k0 + kKeyTile);
       int64_t first = base + T;  // first row of the first non-empty branch that sees key k0
@@ -274,26 +289,22 @@ extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* 
         }
       // main rows r >= k1 - 1 see every key of the tile; so do the rows of
       // every branch from full_b on
-      WorkItem w = make_item(k0, k1 - k0, k0, k1 - 1, base + M, first, base + T, std::max(full_b, first), 0);
-      w.tile_lo = 0;
-      w.tile_hi = int32_t(row_tiles(k0, base + M) + row_tiles(first, base + T));
-      pl->kwork.push_back(w);
+      push_key_item(make_item(k0, k1 - k0, k0, k1 - 1, base + M, first, base + T, std::max(full_b, first), 0),
+                    row_tiles(k0, base + M) + row_tiles(first, base + T));
     }
     for (int64_t k0 = base + M; k0 < base + T; k0 += kKeyTile) {
       const int64_t k1 = std::min(base + T, k0 + kKeyTile);
       int64_t end = k1;  // end of the last branch with a key in [k0, k1)
       for (int32_t k = 0; k < N; ++k)
         if (bstart[k] < k1 && bstart[k] + blen[k] > k0) end = std::max(end, bstart[k] + blen[k]);
-      WorkItem w = make_item(k0, k1 - k0, k0, end, end, 0, 0, 0, kKeyBranch);
-      w.tile_lo = 0;
-      w.tile_hi = int32_t(row_tiles(k0, end));
-      pl->kwork.push_back(w);
+      push_key_item(make_item(k0, k1 - k0, k0, end, end, 0, 0, 0, kKeyBranch), row_tiles(k0, end));
     }
     base += T;
     r += N;
   }
-  std::stable_sort(pl->kwork.begin(), pl->kwork.end(),
-                   [](const WorkItem& x, const WorkItem& y) { return x.tile_hi > y.tile_hi; });
+  std::stable_sort(pl->kwork.begin(), pl->kwork.end(), [](const WorkItem& x, const WorkItem& y) {
+    return x.tile_hi - x.tile_lo > y.tile_hi - y.tile_lo;
+  });
   for (int64_t i = 0; i < total_tokens; ++i) {
     pl->row_a[i] = int32_t(pl->main_end[i]);
     pl->row_b[i] = int32_t(pl->branch_start[i]);

@@ -58,8 +58,20 @@ constexpr int32_t kSegBShared = 8;
 //         B) on see every key of it.  Other row tiles are tested per row
 //         against row_a / row_b: a main key is visible to rows with
 //         key < row_a, a branch key to rows with row_b <= key <= row
-//   tile_hi  number of 64-row tiles walked (cost order)
+//   [tile_lo, tile_hi) the item's 64-row tiles (segment A's, then B's) that
+//         this piece walks; an item whose walk is longer than
+//         kBwdMaxRowTiles is split into near-equal pieces
+//   b_full  partial slot of a split piece (it writes fp32 dK, dV there), or
+//         -1 when the piece is the whole item (it writes dK, dV directly)
 constexpr int32_t kKeyBranch = 2;
+constexpr int64_t kBwdMaxRowTiles = 100;
+
+// A split key tile of the backward: keys [key0, key0 + nkeys) of every KV
+// head sum the fp32 partials of slots [first, first + count), in slot order.
+struct KMerge {
+  int32_t key0, nkeys, first, count;
+};
+static_assert(sizeof(KMerge) == 16, "key merge layout");
 
 // Merge table, one entry per output row combined from partials: slots are
 // sh_first + c * sh_stride (c < sh_count), then sf_first + c * sf_stride
@@ -72,8 +84,8 @@ static_assert(sizeof(MergeRow) == 32, "merge row layout");
 
 // Offsets (bytes) of the tables inside the device workspace.
 struct DeviceLayout {
-  int64_t work = 0, row_a = 0, row_b = 0, mask = 0, merge = 0, kwork = 0, trees = 0, tile_a = 0, tile_b = 0,
-          total = 0;
+  int64_t work = 0, row_a = 0, row_b = 0, mask = 0, merge = 0, kwork = 0, kmerge = 0, trees = 0, tile_a = 0,
+          tile_b = 0, total = 0;
 };
 
 }  // namespace ta
@@ -95,6 +107,8 @@ struct ta_plan {
   std::vector<uint64_t> row_mask;
   std::vector<ta::MergeRow> merge;
   std::vector<ta::WorkItem> kwork;  // prefill: key-major items of the backward
+  std::vector<ta::KMerge> kmerge;   // prefill: key tiles whose backward walk is split
+  int64_t n_kpart = 0;              // partial slots of the split key tiles
   std::vector<int32_t> tree_tab;    // verify: node offsets [n_branches + 1], then parents [n_rows]
   // paged plans: physical cache row of the first token of every 64-token
   // tile of segment A / segment B, indexed by virtual position / 64 (empty

@@ -61,6 +61,8 @@ struct BwdParams {
   float* dd;         // scratch [hq, rows]: sum_d dO * O
   const WorkItem* work;   // row-major items (the forward's)
   const WorkItem* kwork;  // key-major items
+  const KMerge* kmerge;   // split key tiles
+  float* kpart;           // scratch [slots, hkv, 2 (dK, dV), 64 keys, d] fp32 partials
   const int32_t* row_a;
   const int32_t* row_b;
   int32_t hq, hkv, group;
@@ -89,7 +91,7 @@ struct AcceptParams {
 
 hipError_t launch_attention(int mode, int dtype, const AttnParams& p, int n_work, int head_dim, hipStream_t st);
 hipError_t launch_merge(int dtype, const MergeParams& p, int head_dim, hipStream_t st);
-hipError_t launch_backward(const BwdParams& p, int n_work, int n_kwork, int head_dim, hipStream_t st);
+hipError_t launch_backward(const BwdParams& p, int n_work, int n_kwork, int n_kmerge, int head_dim, hipStream_t st);
 hipError_t launch_accept(int dtype, const AcceptParams& p, int64_t n_rows, hipStream_t st);
 
 }  // namespace ta
