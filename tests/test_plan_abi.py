@@ -436,3 +436,28 @@ def test_decode_items_mark_segments_that_several_row_groups_read():
     w1 = synth.config4(with_tensors=False)
     for w in ta.plan_for(w1.desc).export("work"):
         assert int(w[10]) & (4 | 8) == 0
+
+
+def test_backward_scratch_checks_with_split_key_walks():
+    """The backward needs two fp32 values per (query head, row) plus the fp32
+    partial dK, dV of every piece of a split key walk; one byte less is a
+    WORKSPACE error, checked before the plan's upload state."""
+    L = ta.lib()
+    fa = FakeArgs()
+    p = fa.p
+    plan = ta.plan_for(synth.config2(with_tensors=False).desc)
+    rows = plan.info["n_rows"]
+    n_kpart = int((plan.export("bwd_work")[:, 11] >= 0).sum())
+    assert n_kpart > 0
+    hq, hkv, d = 16, 8, 128
+    half = -(-rows * hq * 4 // 256) * 256
+    need = 2 * half + n_kpart * hkv * 2 * 64 * d * 4
+    assert ta.backward_scratch_bytes(plan, hq) >= need
+    bf = ta.TA_DTYPE_BF16
+
+    def call(nbytes):
+        return L.tree_attn_prefill_backward(plan.handle, bf, hq, hkv, d, 0.088, p, p, p, p, p, p, p, p, p, p,
+                                            nbytes, None)
+
+    assert call(need - 1) == ta.TA_ERR_WORKSPACE
+    assert call(need) == ta.TA_ERR_STATE  # valid, but never uploaded
