@@ -236,7 +236,7 @@ struct RowMeta {
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   using T = __bf16;
-  using G = TileGeom<T, D>;
+  using G = TileGeomB<T, D>;
   constexpr int NW = 4;
   constexpr int kKS = D / 32;  // k-steps of 32 over head_dim
   constexpr int kDB = D / 16;  // 16-wide blocks of head_dim
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
   auto rt0 = [&](int r) { return r < n_a ? wi.a_lo + r * kKeyTile : wi.b_lo + (r - n_a) * kKeyTile; };
   auto rt_hi = [&](int r) { return r < n_a ? wi.a_hi : wi.b_hi; };
 
-  TileLoader<T, D, NW> loader;
+  TileLoader<T, D, NW, 0, G> loader;
   loader.init(lane, wave, q_stride);
   // step s = (query head j of the group, row tile r of the piece): Q and dO
   // tiles go to the stage by DMA; the row values by wave 0, through registers

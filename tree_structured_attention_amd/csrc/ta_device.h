@@ -92,14 +92,36 @@ struct TileGeom {
   }
 };
 
+// The same tile for 16x16x32 operand reads (the key-major backward): there
+// a transposing read gives lane group g rows 4 g .. 4 g + 3 of a 16-row block
+// at 16 consecutive d (one chunk pair), and groups g, g + 1 are served
+// together, so rows r and r + 4 must not share banks for a chunk pair:
+//   swz(row) = 2 ((row / P) mod (chunks / 2)) + (row / 8) mod 2,
+// with P rows per 256-byte bank period.  The 16 rows of a 16x16x32 operand
+// read still land in distinct chunk positions of their bank period.
+template <typename T, int D>
+struct TileGeomB {
+  static constexpr int kRowBytes = D * Elt<T>::kBytes;
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kTileBytes = kKeyTile * kRowBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes;
+  static constexpr int kPeriod = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
+  __device__ static __forceinline__ int swz(int row) {
+    return ((((row / kPeriod) & (kChunks / 2 - 1)) << 1) | ((row >> 3) & 1)) & (kChunks - 1);
+  }
+  __device__ static __forceinline__ int at(int row, int byte) {
+    return row * kRowBytes + ((((byte >> 4) ^ swz(row)) << 4) | (byte & 15));
+  }
+};
+
 // Global -> LDS copy of one 64-key K/V tile with buffer loads that write LDS
 // directly.  The buffer resource covers only the keys of the segment still
 // to be read, so rows past its end load as zeros (no branches).  CPOL is the
 // loads' cache policy (kCpolStream for data no other workgroup reads again).
 constexpr int kCpolStream = 2;  // nt: non-temporal
-template <typename T, int D, int NW, int CPOL = 0>
+template <typename T, int D, int NW, int CPOL = 0, typename Geom = TileGeom<T, D>>
 struct TileLoader {
-  using G = TileGeom<T, D>;
+  using G = Geom;
   static constexpr int kRowsPerInst = 64 / G::kChunks;
   static constexpr int kInsts = kKeyTile / (kRowsPerInst * NW);
   static_assert(kInsts * kRowsPerInst * NW == kKeyTile, "tile split");
