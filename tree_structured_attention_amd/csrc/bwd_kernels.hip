@@ -216,7 +216,8 @@ __global__ __launch_bounds__(128 * GH, 2) void bwd_dq_kernel(BwdParams p) {
 // dK, dV: key-major
 // ---------------------------------------------------------------------------
 
-// Per-row values of a 64-row tile staged beside its Q and dO tiles.
+// Per-row values of a 64-row tile staged beside its Q and dO tiles (four
+// 256-byte arrays, one DMA each).
 struct RowMeta {
   float l2[64], dd[64];
   int32_t ra[64], rb[64];
@@ -258,43 +259,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
 
   TileLoader<T, D, NW, 0, G> loader;
   loader.init(lane, wave, q_stride);
-  // step s = (query head j of the group, row tile r of the piece): Q and dO
-  // tiles go to the stage by DMA; the row values by wave 0, through registers
+  // step s = (query head j of the group, row tile r of the piece): the Q and
+  // dO tiles and the tile's row values go to the stage by DMA; wave w copies
+  // row-value array w of RowMeta (lse2, Dd, row_a, row_b), and rows past the
+  // segment end read as 0
   auto issue = [&](int s, unsigned char* stage) {
     const int j = s / n_pc, r = wi.tile_lo + s % n_pc;
     const int head = kvh * p.group + j;
     const unsigned char* qb = reinterpret_cast<const unsigned char*>(p.q) + int64_t(head) * D * 2;
     const unsigned char* gb = reinterpret_cast<const unsigned char*>(p.dO) + int64_t(head) * D * 2;
-    loader.issue(stage, qb, gb, rt0(r), rt_hi(r), q_stride, wave);
-  };
-  auto load_meta = [&](int s, float4& a, float4& b, int4& c, int4& d) {
-    const int j = s / n_pc, r = wi.tile_lo + s % n_pc;
-    const int head = kvh * p.group + j;
-    const int r0 = rt0(r), rhi = min(rt_hi(r), r0 + kKeyTile);
-    const int x = r0 + 4 * (lane & 15);
+    const int r0 = rt0(r), rhi = rt_hi(r);
+    loader.issue(stage, qb, gb, r0, rhi, q_stride, wave);
     const int64_t hb = int64_t(head) * p.n_rows;
-    float l[4], e[4];
-    int u[4], w[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const bool ok = x + t < rhi;
-      l[t] = ok ? p.l2[hb + x + t] : 0.f;
-      e[t] = ok ? p.dd[hb + x + t] : 0.f;
-      u[t] = ok ? p.row_a[x + t] : 0;
-      w[t] = ok ? p.row_b[x + t] : 0;
-    }
-    a = make_float4(l[0], l[1], l[2], l[3]);
-    b = make_float4(e[0], e[1], e[2], e[3]);
-    c = make_int4(u[0], u[1], u[2], u[3]);
-    d = make_int4(w[0], w[1], w[2], w[3]);
-  };
-  auto store_meta = [&](unsigned char* stage, const float4& a, const float4& b, const int4& c, const int4& d) {
-    RowMeta* m = reinterpret_cast<RowMeta*>(stage + G::kStageBytes);
-    const int x = 4 * (lane & 15);
-    *reinterpret_cast<float4*>(&m->l2[x]) = a;
-    *reinterpret_cast<float4*>(&m->dd[x]) = b;
-    *reinterpret_cast<int4*>(&m->ra[x]) = c;
-    *reinterpret_cast<int4*>(&m->rb[x]) = d;
+    const void* src = wave == 0   ? static_cast<const void*>(p.l2 + hb + r0)
+                      : wave == 1 ? static_cast<const void*>(p.dd + hb + r0)
+                      : wave == 2 ? static_cast<const void*>(p.row_a + r0)
+                                  : static_cast<const void*>(p.row_b + r0);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), (short)0, 4 * min(rhi - r0, kKeyTile), 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + G::kStageBytes + 4 * kKeyTile * wave), 4,
+                                             4 * lane, 0, 0, 0);
   };
 
   // this wave's 16 keys as B operands (lane: key l % 16, dims 32 ks + 8 g ..)
@@ -405,25 +389,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  float4 ma, mb;
-  int4 mc, md4;
-  if (n_steps > 0) {
-    issue(0, lds0);
-    if (wave == 0) {
-      load_meta(0, ma, mb, mc, md4);
-      store_meta(lds0, ma, mb, mc, md4);
-    }
-  }
+  if (n_steps > 0) issue(0, lds0);
   auto step = [&](int s, unsigned char* cur, unsigned char* nxt) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies into cur are done
     __syncthreads();                     // ... and every wave's; reads of nxt are retired
-    const bool more = s + 1 < n_steps;
-    if (more) {
-      issue(s + 1, nxt);
-      if (wave == 0) load_meta(s + 1, ma, mb, mc, md4);
-    }
+    if (s + 1 < n_steps) issue(s + 1, nxt);
     consume(cur, s);
-    if (more && wave == 0) store_meta(nxt, ma, mb, mc, md4);
   };
 #pragma unroll 1
   for (int s = 0; s < n_steps; s += 2) {
