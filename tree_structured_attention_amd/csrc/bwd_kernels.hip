@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
         pd[2 * b1] = pack_bf16x2(ds[0], ds[1]);
         pd[2 * b1 + 1] = pack_bf16x2(ds[2], ds[3]);
       }
-      sched_ld_mfma<0, 4 * kKS, 1, 4>();
+      sched_ld_mfma<0, 4 * kKS, 1, 8>();
       // dV^T += dO^T P and dK^T += Q^T dS over these 32 rows
       const bf16x8 bp = __builtin_bit_cast(bf16x8, pp);
       const bf16x8 bd = __builtin_bit_cast(bf16x8, pd);
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
         const s16x4 qq[2] = {q0, q1};
         dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qq), bd, dk[db], 0, 0, 0);
       }
-      sched_ld_mfma<0, 2 * kDB, 2, 8>();
+      sched_ld_mfma<0, 2 * kDB, 2, 16>();
     }
   };
 
