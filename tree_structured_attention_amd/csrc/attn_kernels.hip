@@ -146,8 +146,11 @@ struct RowState {
       if (__any(m_used == -INFINITY)) rebase(s, false);
       u32x4 pw[2][2];
       float ls = exp_pack(s, pw);
-      if (__any(pair_max(ls) > 65536.f)) {
-        rebase(s, true);
+      // the decision is the row's own (both lanes of a row see the same
+      // pair maximum); __any only skips the branch when no row needs it
+      const bool over = pair_max(ls) > 65536.f;
+      if (__any(over)) {
+        rebase(s, over);
         ls = exp_pack(s, pw);
       }
       l_run += ls;
@@ -219,17 +222,17 @@ struct RowState {
     }
   }
 
-  // bf16: move each row's base to its maximum so far -- only rows that have
-  // none yet, or with `all` every row whose maximum grew; O and l scale by
-  // the change.
-  __device__ __forceinline__ void rebase(const f32x16 (&s)[2], bool all) {
+  // bf16: move a row's base to its maximum so far if the row has none yet,
+  // or if `sel` (this row's own choice) is set and its maximum grew; O and l
+  // scale by the change.  Every other row keeps its base and its bits.
+  __device__ __forceinline__ void rebase(const f32x16 (&s)[2], bool sel) {
     float mt = s[0][0];
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[bk][i]);
     mt = pair_max(mt);
-    const bool grow = (all || m_used == -INFINITY) && mt > m_used;
+    const bool grow = (sel || m_used == -INFINITY) && mt > m_used;
     const float m_new = grow ? mt : m_used;
     const float alpha = (grow && m_used != -INFINITY) ? fast_exp2((m_used - m_new) * c) : 1.f;
     l_run *= alpha;
