@@ -17,7 +17,9 @@
  *    On error nothing is enqueued, no output is written (except the sizes
  *    tree_attn_plan_export and tree_attn_pool_table report along with
  *    TA_ERR_WORKSPACE), and tree_attn_last_error() (thread-local) explains.
- *    No exception crosses the ABI.
+ *    No exception crosses the ABI: a host allocation failure inside any call
+ *    returns TA_ERR_CAPACITY ("out of host memory") and leaves every object
+ *    passed in as it was.
  *  - Memory: the caller allocates all device memory (tensors, plan workspace,
  *    scratch, paged caches).  The library allocates only host memory for
  *    plans and block pools.
@@ -25,7 +27,9 @@
  *    stream).  Calls only enqueue; none synchronizes the host except
  *    tree_attn_plan_destroy (waits for the plan's pending upload).  Device
  *    faults surface at the caller's next synchronization.  Buffers must stay
- *    alive until the stream has passed the call.
+ *    alive until the stream has passed the call.  A launch reads the plan's
+ *    device tables without waiting for tree_attn_plan_upload's copy: launch
+ *    on the upload's stream, or order the two streams yourself.
  *  - Layouts (all contiguous, head_dim fastest, 16-byte aligned):
  *      q, o : [rows,   Hq,  head_dim]      k, v : [tokens, Hkv, head_dim]
  *      lse  : [Hq, rows] float32, natural-log log-sum-exp of the scaled
@@ -87,6 +91,16 @@ extern "C" {
                                            every row; decode: 4 / 8: segment A / B also read by other items, so its
                                            copies keep the default cache policy) (diagnostic; order is not
                                            contractual) */
+#define TA_FIELD_DEVICE_LAYOUT 12 /* any: [11] byte offsets of the sections of the device image that
+                                     tree_attn_plan_upload copies: work list (48 B items), row_a (int32),
+                                     row_b (int32), row_mask (uint64), merge table (32 B rows), backward
+                                     key-major items, backward key merges, tree table (int32), paged tiles
+                                     of A and of B (int32); then the image's total bytes.  row_a / row_b
+                                     hold per row: prefill main_end / branch_start; decode the absolute end
+                                     of its main keys / of its suffix keys; verify the end of its page's
+                                     context / its tree's first node (row_mask: its ancestor bitmask) */
+#define TA_FIELD_DEVICE_IMAGE 13  /* any: the device image itself, 8 bytes per int64 entry (little endian),
+                                     byte for byte what tree_attn_plan_upload copies to the workspace */
 
 typedef struct ta_plan ta_plan; /* opaque, host-owned, immutable once built */
 
@@ -292,7 +306,9 @@ int tree_attn_plan_balance(ta_plan* plan, int32_t n_kv_heads, int32_t n_slots);
 /* Enqueue the asynchronous copy of the plan's device tables into
  * dev_workspace (>= info.workspace_bytes bytes, 256-byte aligned, caller
  * owned) on `stream`, and bind the plan to that workspace.  Kernels launched
- * afterwards read only the workspace.  May be called again to rebind. */
+ * afterwards read only the workspace; launches must follow the copy in
+ * stream order (same stream, or ordered by the caller).  May be called
+ * again to rebind. */
 int tree_attn_plan_upload(ta_plan* plan, void* dev_workspace, size_t bytes, void* stream);
 
 /* Wait for a pending upload, then free the host plan.  NULL is a no-op. */

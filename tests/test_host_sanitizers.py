@@ -19,7 +19,8 @@ def test_host_code_under_sanitizers(tmp_path):
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-fno-omit-frame-pointer", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
            os.path.join(HERE, "host_fuzz", "fuzz.cpp"), os.path.join(HERE, "host_fuzz", "stub.cpp"),
-           os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "draft.cpp"), os.path.join(CSRC, "kv_pool.cpp"),
+           os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "errors.cpp"), os.path.join(CSRC, "draft.cpp"),
+           os.path.join(CSRC, "kv_pool.cpp"),
            "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0 and "sanitizer" in (r.stderr or "").lower() and "cannot find" in r.stderr:

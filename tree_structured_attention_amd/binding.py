@@ -12,6 +12,7 @@ Names mirror the C entry points without the ``tree_attn_`` prefix:
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -51,6 +52,8 @@ FIELD = {
     "work": 9,
     "bwd_work": 10,
     "paged_tiles": 11,
+    "device_layout": 12,
+    "device_image": 13,
 }
 FIELD_WIDTH = {"pages": 5, "branches": 3, "decode_rows": 5, "verify_rows": 4, "work": 11, "bwd_work": 12}
 
@@ -296,12 +299,14 @@ def plan_upload(plan: Plan, device=None, stream=None) -> Plan:
     """Allocate the device workspace with torch and enqueue the plan copy."""
     nbytes = plan_info(plan)["workspace_bytes"]
     dev = torch.device("cuda" if device is None else device)
-    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    with _on(stream):
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
     off = (-ws.data_ptr()) % 256
     ws_view = ws[off: off + nbytes]
     _check(lib().tree_attn_plan_upload(plan.handle, ctypes.c_void_p(ws_view.data_ptr()), nbytes,
                                        _stream_handle(stream)))
     plan.workspace = ws
+    plan.workspace_view = ws_view
     return plan
 
 
@@ -316,15 +321,17 @@ def scratch_bytes(plan: Plan, hq: int, head_dim: int) -> int:
 
 
 def _scratch(plan, hq, d, device, scratch):
-    """Caller-provided scratch (uint8 tensor) or a fresh one; 256-byte aligned view."""
+    """Caller-provided scratch (uint8 tensor) or a fresh one; returns the
+    256-byte aligned pointer, its usable bytes and the tensor to keep alive
+    across the call."""
     need = scratch_bytes(plan, hq, d)
     if need == 0:
-        return None, 0
+        return None, 0, None
     if scratch is None:
         scratch = torch.empty(need + 256, dtype=torch.uint8, device=device)
     off = (-scratch.data_ptr()) % 256
     view = scratch[off:]
-    return ctypes.c_void_p(view.data_ptr()), view.numel()
+    return ctypes.c_void_p(view.data_ptr()), view.numel(), scratch
 
 
 # ---------------------------------------------------------------------------
@@ -349,10 +356,77 @@ def _dev_ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _heads(q: torch.Tensor, k: torch.Tensor):
-    if q.dim() != 3 or k.dim() != 3:
-        raise TreeAttnError(TA_ERR_INVALID_ARG, "q is [rows, Hq, d] and k/v are [tokens, Hkv, d]")
-    return q.shape[1], k.shape[1], q.shape[2]
+def _bad(msg):
+    return TreeAttnError(TA_ERR_INVALID_ARG, msg)
+
+
+def _check_args(q, kv_pairs, out=None, lse=None, like_q=(), like_kv=()):
+    """Host-side checks of every tensor argument before any pointer is taken.
+
+    The C ABI receives raw pointers and sizes (hq, hkv, head_dim) derived
+    from q and the first key tensor, so a tensor of another dtype, head
+    count, head_dim or an undersized output would be read or written out of
+    bounds on the device.  Checked here: q is [rows, Hq, d]; each (k, v)
+    pair is [tokens, Hkv, d] with v shaped like k; every tensor has q's
+    dtype and device and is contiguous; `out` and the tensors in `like_q`
+    are shaped like q, those in `like_kv` like the first key tensor; `lse`
+    is fp32 [Hq, rows].  Returns (hq, hkv, d)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise _bad("q is [rows, Hq, d]")
+    _dtype_code(q)
+    rows, hq, d = q.shape
+    named = [("q", q)]
+    hkv = kshape = None
+    for (kn, k), (vn, v) in kv_pairs:
+        if k is None or v is None:
+            raise _bad(f"{kn} and {vn} are required")
+        if k.dim() != 3:
+            raise _bad(f"{kn} is [tokens, Hkv, d]")
+        if tuple(v.shape) != tuple(k.shape):
+            raise _bad(f"{vn} {tuple(v.shape)} must have the shape of {kn} {tuple(k.shape)}")
+        if k.shape[2] != d:
+            raise _bad(f"{kn} has head_dim {k.shape[2]}; q has {d}")
+        if hkv is None:
+            hkv, kshape = k.shape[1], tuple(k.shape)
+        elif k.shape[1] != hkv:
+            raise _bad(f"{kn} has {k.shape[1]} KV heads; the first key tensor has {hkv}")
+        named += [(kn, k), (vn, v)]
+    for name, t in like_q:
+        if t is not None and tuple(t.shape) != tuple(q.shape):
+            raise _bad(f"{name} {tuple(t.shape)} must have the shape of q {tuple(q.shape)}")
+        named.append((name, t))
+    for name, t in like_kv:
+        if t is not None and tuple(t.shape) != kshape:
+            raise _bad(f"{name} {tuple(t.shape)} must have the shape of the key tensor {kshape}")
+        named.append((name, t))
+    if out is not None:
+        if tuple(out.shape) != tuple(q.shape):
+            raise _bad(f"out {tuple(out.shape)} must have the shape of q {tuple(q.shape)}")
+        named.append(("out", out))
+    for name, t in named:
+        if t is None:
+            continue
+        if t.dtype != q.dtype:
+            raise _bad(f"{name} is {t.dtype}; q is {q.dtype} (all tensors share one dtype)")
+        if t.device != q.device:
+            raise _bad(f"{name} is on {t.device}; q is on {q.device}")
+        if not t.is_contiguous():
+            raise _bad(f"{name} must be contiguous")
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (hq, rows):
+            raise _bad(f"lse must be float32 [Hq, rows] = [{hq}, {rows}]; got {lse.dtype} {tuple(lse.shape)}")
+        if lse.device != q.device or not lse.is_contiguous():
+            raise _bad("lse must be contiguous on q's device")
+    return hq, hkv, d
+
+
+def _check_scratch_tensor(scratch, device):
+    if scratch is None:
+        return
+    if scratch.dtype != torch.uint8 or scratch.dim() != 1 or not scratch.is_contiguous():
+        raise _bad("scratch is a contiguous 1-D uint8 tensor")
+    if scratch.device != device:
+        raise _bad(f"scratch is on {scratch.device}; the inputs are on {device}")
 
 
 def _rows(plan: Plan, q, seg_a=(), seg_b=()):
@@ -372,6 +446,13 @@ def _rows(plan: Plan, q, seg_a=(), seg_b=()):
                                                     f"{info['n_keys_b']}")
 
 
+def _on(stream):
+    """Allocate temporaries on the stream the launch uses, so torch's caching
+    allocator does not hand their memory to other work while the kernels
+    still run there."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _outputs(q, want_lse, out=None, lse=None):
     if out is None:
         out = torch.empty_like(q)
@@ -386,10 +467,12 @@ def _scale(scale, d):
 
 def prefill(plan: Plan, q, k, v, scale=None, want_lse=True, out=None, lse=None,
             scratch: Optional[torch.Tensor] = None, stream=None):
-    hq, hkv, d = _heads(q, k)
+    hq, hkv, d = _check_args(q, [(("k", k), ("v", v))], out=out, lse=lse)
+    _check_scratch_tensor(scratch, q.device)
     _rows(plan, q, (k, v), (k, v))
-    o, l = _outputs(q, want_lse, out, lse)
-    sp, sn = _scratch(plan, hq, d, q.device, scratch)
+    with _on(stream):
+        o, l = _outputs(q, want_lse, out, lse)
+        sp, sn, keep = _scratch(plan, hq, d, q.device, scratch)
     _check(lib().tree_attn_prefill(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
                                    _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(l), sp, sn,
                                    _stream_handle(stream)))
@@ -398,10 +481,13 @@ def prefill(plan: Plan, q, k, v, scale=None, want_lse=True, out=None, lse=None,
 
 def decode(plan: Plan, q, k_main, v_main, k_suffix, v_suffix, scale=None, want_lse=True, out=None, lse=None,
            scratch: Optional[torch.Tensor] = None, stream=None):
-    hq, hkv, d = _heads(q, k_main)
+    hq, hkv, d = _check_args(q, [(("k_main", k_main), ("v_main", v_main)),
+                                 (("k_suffix", k_suffix), ("v_suffix", v_suffix))], out=out, lse=lse)
+    _check_scratch_tensor(scratch, q.device)
     _rows(plan, q, (k_main, v_main), (k_suffix, v_suffix))
-    o, l = _outputs(q, want_lse, out, lse)
-    sp, sn = _scratch(plan, hq, d, q.device, scratch)
+    with _on(stream):
+        o, l = _outputs(q, want_lse, out, lse)
+        sp, sn, keep = _scratch(plan, hq, d, q.device, scratch)
     _check(lib().tree_attn_decode(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
                                   _dev_ptr(k_main), _dev_ptr(v_main), _dev_ptr(k_suffix), _dev_ptr(v_suffix),
                                   _dev_ptr(o), _dev_ptr(l), sp, sn, _stream_handle(stream)))
@@ -410,10 +496,13 @@ def decode(plan: Plan, q, k_main, v_main, k_suffix, v_suffix, scale=None, want_l
 
 def verify(plan: Plan, q, k_ctx, v_ctx, k_tree, v_tree, scale=None, want_lse=True, out=None, lse=None,
            scratch: Optional[torch.Tensor] = None, stream=None):
-    hq, hkv, d = _heads(q, k_ctx)
+    hq, hkv, d = _check_args(q, [(("k_ctx", k_ctx), ("v_ctx", v_ctx)), (("k_tree", k_tree), ("v_tree", v_tree))],
+                             out=out, lse=lse)
+    _check_scratch_tensor(scratch, q.device)
     _rows(plan, q, (k_ctx, v_ctx), (k_tree, v_tree))
-    o, l = _outputs(q, want_lse, out, lse)
-    sp, sn = _scratch(plan, hq, d, q.device, scratch)
+    with _on(stream):
+        o, l = _outputs(q, want_lse, out, lse)
+        sp, sn, keep = _scratch(plan, hq, d, q.device, scratch)
     _check(lib().tree_attn_verify(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
                                   _dev_ptr(k_ctx), _dev_ptr(v_ctx), _dev_ptr(k_tree), _dev_ptr(v_tree),
                                   _dev_ptr(o), _dev_ptr(l), sp, sn, _stream_handle(stream)))
@@ -430,16 +519,21 @@ def prefill_backward(plan: Plan, q, k, v, o, lse, d_o, scale=None, dq=None, dk=N
                      scratch: Optional[torch.Tensor] = None, stream=None):
     """Gradients (dq, dk, dv) of the packed forward for output gradient d_o;
     o and lse are the forward's outputs for the same q, k, v."""
-    hq, hkv, d = _heads(q, k)
-    _rows(plan, q, (k, v, o, d_o, dk, dv), (k, v))
-    if d_o.shape[0] != q.shape[0] or o.shape[0] != q.shape[0] or (dq is not None and dq.shape[0] != q.shape[0]):
-        raise TreeAttnError(TA_ERR_INVALID_ARG, "o, d_o and dq need one row per query row")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    if o is None or d_o is None or lse is None:
+        raise _bad("o, lse and d_o are required")
+    hq, hkv, d = _check_args(q, [(("k", k), ("v", v))], lse=lse,
+                             like_q=(("o", o), ("d_o", d_o), ("dq", dq)), like_kv=(("dk", dk), ("dv", dv)))
+    if k.shape[0] != q.shape[0]:
+        raise _bad(f"k has {k.shape[0]} tokens; the packed prefill has one key per query row ({q.shape[0]})")
+    _check_scratch_tensor(scratch, q.device)
+    _rows(plan, q, (k, v), (k, v))
     need = backward_scratch_bytes(plan, hq)
-    if scratch is None and need:
-        scratch = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    with _on(stream):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        if scratch is None and need:
+            scratch = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
     sp, sn = None, 0
     if need:
         off = (-scratch.data_ptr()) % 256
@@ -506,12 +600,18 @@ def accept(plan: Plan, logits, tokens, tau: float = 0.75, exact: bool = False, v
         if t is not None and (t.dtype != torch.int32 or t.numel() < n):
             raise TreeAttnError(TA_ERR_INVALID_ARG, f"{name} must be int32 with at least {n} entries")
     dev = logits.device
-    path = torch.zeros(max(n_nodes, 1), dtype=torch.int32, device=dev) if path is None else path
-    n_path = torch.empty(max(n_trees, 1), dtype=torch.int32, device=dev) if n_path is None else n_path
-    next_token = torch.empty(max(n_trees, 1), dtype=torch.int32, device=dev) if next_token is None else next_token
+    for name, t in (("logits", logits), ("tokens", tokens), ("path", path), ("n_path", n_path),
+                    ("next_token", next_token)):
+        if t is not None and (t.device != dev or not t.is_contiguous()):
+            raise _bad(f"{name} must be contiguous on the logits' device")
+    _check_scratch_tensor(scratch, dev)
     need = accept_scratch_bytes(plan, vocab)
-    if scratch is None:
-        scratch = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    with _on(stream):
+        path = torch.zeros(max(n_nodes, 1), dtype=torch.int32, device=dev) if path is None else path
+        n_path = torch.empty(max(n_trees, 1), dtype=torch.int32, device=dev) if n_path is None else n_path
+        next_token = torch.empty(max(n_trees, 1), dtype=torch.int32, device=dev) if next_token is None else next_token
+        if scratch is None:
+            scratch = torch.empty(need + 256, dtype=torch.uint8, device=dev)
     off = (-scratch.data_ptr()) % 256
     view = scratch[off:]
     _check(lib().tree_attn_accept(plan.handle, _dtype_code(logits), _dev_ptr(logits), vocab, ld, _dev_ptr(tokens),

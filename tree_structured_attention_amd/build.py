@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtree_attn.so")
 
 ARCH = os.environ.get("TREE_ATTN_ARCH", "gfx950")
-HOST_SOURCES = ["plan.cpp", "api.cpp", "draft.cpp", "kv_pool.cpp"]
+HOST_SOURCES = ["plan.cpp", "api.cpp", "errors.cpp", "draft.cpp", "kv_pool.cpp"]
 HIP_SOURCES = ["attn_kernels.hip", "bwd_kernels.hip", "accept_kernels.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]
 # Packed fp32 VALU ops are kept out of the device code on purpose.

@@ -6,21 +6,15 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
+#include <new>
+#include <stdexcept>
 #include <string>
 
 #include "ta_kernels.h"
 
 namespace ta {
-
-static thread_local std::string g_last_error;
-
-void set_error(const std::string& msg) { g_last_error = msg; }
-
-int fail(int code, const std::string& msg) {
-  g_last_error = msg;
-  return code;
-}
 
 namespace {
 
@@ -119,11 +113,9 @@ hipError_t launch_merge_for(const ta_plan* plan, int dtype, const AttnParams& p,
 
 using namespace ta;
 
-extern "C" const char* tree_attn_last_error(void) { return g_last_error.c_str(); }
-
 extern "C" const char* tree_attn_version(void) { return "tree_attn 0.1 gfx950"; }
 
-extern "C" int tree_attn_plan_info(const ta_plan* plan, ta_plan_info* out) {
+extern "C" int tree_attn_plan_info(const ta_plan* plan, ta_plan_info* out) try {
   if (!plan || !out) return fail(TA_ERR_INVALID_ARG, "plan_info: NULL argument");
   out->kind = plan->kind;
   out->n_pages = plan->n_pages;
@@ -137,10 +129,12 @@ extern "C" int tree_attn_plan_info(const ta_plan* plan, ta_plan_info* out) {
   out->visible_pairs = plan->visible_pairs;
   out->max_depth = plan->max_depth;
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("plan_info");
 }
 
 extern "C" int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t* dst, int64_t cap,
-                                     int64_t* n_written) {
+                                     int64_t* n_written) try {
   if (!plan || !n_written) return fail(TA_ERR_INVALID_ARG, "plan_export: NULL argument");
   std::vector<int64_t> work_tmp;
   const std::vector<int64_t>* src = nullptr;
@@ -167,6 +161,17 @@ extern "C" int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t
       work_tmp.insert(work_tmp.end(), plan->tile_b.begin(), plan->tile_b.end());
       src = &work_tmp;
       break;
+    case TA_FIELD_DEVICE_LAYOUT: {
+      const DeviceLayout& L = plan->layout;
+      work_tmp = {L.work, L.row_a, L.row_b, L.mask, L.merge, L.kwork, L.kmerge, L.trees, L.tile_a, L.tile_b, L.total};
+      src = &work_tmp;
+      break;
+    }
+    case TA_FIELD_DEVICE_IMAGE:
+      work_tmp.resize(plan->blob.size() / sizeof(int64_t));
+      if (!work_tmp.empty()) std::memcpy(work_tmp.data(), plan->blob.data(), work_tmp.size() * sizeof(int64_t));
+      src = &work_tmp;
+      break;
     case TA_FIELD_WORK:
       for (const WorkItem& w : plan->work)
         work_tmp.insert(work_tmp.end(), {w.row0, w.nrows, w.a_lo, w.a_full, w.a_hi, w.b_lo, w.b_hi, w.out,
@@ -183,9 +188,11 @@ extern "C" int tree_attn_plan_export(const ta_plan* plan, int32_t field, int64_t
     std::memcpy(dst, src->data(), src->size() * sizeof(int64_t));
   }
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("plan_export");
 }
 
-extern "C" int tree_attn_plan_upload(ta_plan* plan, void* dev_workspace, size_t bytes, void* stream) {
+extern "C" int tree_attn_plan_upload(ta_plan* plan, void* dev_workspace, size_t bytes, void* stream) try {
   if (!plan) return fail(TA_ERR_INVALID_ARG, "plan_upload: plan is NULL");
   if (!dev_workspace) return fail(TA_ERR_WORKSPACE, "plan_upload: workspace is NULL");
   if (!aligned(dev_workspace, 256)) return fail(TA_ERR_INVALID_ARG, "plan_upload: workspace must be 256-byte aligned");
@@ -204,6 +211,8 @@ extern "C" int tree_attn_plan_upload(ta_plan* plan, void* dev_workspace, size_t 
   if (e != hipSuccess) return hip_status(e, "plan_upload");
   plan->dev = dev_workspace;
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("plan_upload");
 }
 
 extern "C" void tree_attn_plan_destroy(ta_plan* plan) {
@@ -217,16 +226,18 @@ extern "C" void tree_attn_plan_destroy(ta_plan* plan) {
   delete plan;
 }
 
-extern "C" int tree_attn_scratch_bytes(const ta_plan* plan, int32_t hq, int32_t head_dim, size_t* bytes) {
+extern "C" int tree_attn_scratch_bytes(const ta_plan* plan, int32_t hq, int32_t head_dim, size_t* bytes) try {
   if (!plan || !bytes) return fail(TA_ERR_INVALID_ARG, "scratch_bytes: NULL argument");
   if (hq <= 0 || head_dim <= 0) return fail(TA_ERR_INVALID_ARG, "scratch_bytes: hq and head_dim must be positive");
   *bytes = size_t(scratch_need(plan, hq, head_dim));
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("scratch_bytes");
 }
 
 extern "C" int tree_attn_prefill(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim,
                                  float scale, const void* q, const void* k, const void* v, void* o, float* lse,
-                                 void* scratch, size_t scratch_bytes, void* stream) {
+                                 void* scratch, size_t scratch_bytes, void* stream) try {
   int rc = check_plan(plan, TA_PLAN_PREFILL, "prefill");
   if (rc) return rc;
   if ((rc = check_heads(dtype, hq, hkv, head_dim, scale))) return rc;
@@ -248,12 +259,14 @@ extern "C" int tree_attn_prefill(const ta_plan* plan, int32_t dtype, int32_t hq,
   rc = hip_status(launch_attention(kPrefill, dtype, p, int(plan->work.size()), head_dim, st), "prefill launch");
   if (rc) return rc;
   return hip_status(launch_merge_for(plan, dtype, p, head_dim, st), "prefill merge launch");
+} catch (...) {
+  return ta::fail_exception("prefill");
 }
 
 extern "C" int tree_attn_verify(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim,
                                 float scale, const void* q, const void* k_ctx, const void* v_ctx, const void* k_tree,
                                 const void* v_tree, void* o, float* lse, void* scratch, size_t scratch_bytes,
-                                void* stream) {
+                                void* stream) try {
   int rc = check_plan(plan, TA_PLAN_VERIFY, "verify");
   if (rc) return rc;
   if ((rc = check_heads(dtype, hq, hkv, head_dim, scale))) return rc;
@@ -278,12 +291,14 @@ extern "C" int tree_attn_verify(const ta_plan* plan, int32_t dtype, int32_t hq, 
   rc = hip_status(launch_attention(kVerify, dtype, p, int(plan->work.size()), head_dim, st), "verify launch");
   if (rc) return rc;
   return hip_status(launch_merge_for(plan, dtype, p, head_dim, st), "verify merge launch");
+} catch (...) {
+  return ta::fail_exception("verify");
 }
 
 extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim,
                                 float scale, const void* q, const void* k_main, const void* v_main,
                                 const void* k_suffix, const void* v_suffix, void* o, float* lse, void* scratch,
-                                size_t scratch_bytes, void* stream) {
+                                size_t scratch_bytes, void* stream) try {
   int rc = check_plan(plan, TA_PLAN_DECODE, "decode");
   if (rc) return rc;
   if ((rc = check_heads(dtype, hq, hkv, head_dim, scale))) return rc;
@@ -308,6 +323,8 @@ extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, 
   rc = hip_status(launch_attention(kDecode, dtype, p, int(plan->work.size()), head_dim, st), "decode launch");
   if (rc) return rc;
   return hip_status(launch_merge_for(plan, dtype, p, head_dim, st), "decode merge launch");
+} catch (...) {
+  return ta::fail_exception("decode");
 }
 
 namespace {
@@ -319,18 +336,20 @@ int64_t kpart_bytes(const ta_plan* plan, int64_t hkv, int64_t head_dim) {
 
 }  // namespace
 
-extern "C" int tree_attn_backward_scratch_bytes(const ta_plan* plan, int32_t hq, size_t* bytes) {
+extern "C" int tree_attn_backward_scratch_bytes(const ta_plan* plan, int32_t hq, size_t* bytes) try {
   if (!plan || !bytes) return fail(TA_ERR_INVALID_ARG, "backward_scratch_bytes: NULL argument");
   if (hq <= 0) return fail(TA_ERR_INVALID_ARG, "backward_scratch_bytes: hq must be positive");
   // the partials are sized for the largest call: Hkv <= Hq, head_dim <= 128
   *bytes = size_t(2 * align256(plan->n_rows * hq * 4) + kpart_bytes(plan, hq, 128));
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("backward_scratch_bytes");
 }
 
 extern "C" int tree_attn_prefill_backward(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
                                           int32_t head_dim, float scale, const void* q, const void* k, const void* v,
                                           const void* o, const float* lse, const void* d_o, void* dq, void* dk,
-                                          void* dv, void* scratch, size_t scratch_bytes, void* stream) {
+                                          void* dv, void* scratch, size_t scratch_bytes, void* stream) try {
   int rc = check_plan(plan, TA_PLAN_PREFILL, "prefill_backward");
   if (rc) return rc;
   if ((rc = check_heads(dtype, hq, hkv, head_dim, scale))) return rc;
@@ -380,6 +399,8 @@ extern "C" int tree_attn_prefill_backward(const ta_plan* plan, int32_t dtype, in
   return hip_status(launch_backward(p, int(plan->work.size()), int(plan->kwork.size()), int(plan->kmerge.size()),
                                     head_dim, static_cast<hipStream_t>(stream)),
                     "prefill_backward launch");
+} catch (...) {
+  return ta::fail_exception("prefill_backward");
 }
 
 namespace ta {
@@ -404,7 +425,7 @@ int64_t accept_rows(const ta_plan* plan) { return plan->n_rows + plan->n_branche
 }  // namespace
 }  // namespace ta
 
-extern "C" int tree_attn_accept_scratch_bytes(const ta_plan* plan, int64_t vocab, size_t* bytes) {
+extern "C" int tree_attn_accept_scratch_bytes(const ta_plan* plan, int64_t vocab, size_t* bytes) try {
   if (!plan || !bytes) return fail(TA_ERR_INVALID_ARG, "accept_scratch_bytes: NULL argument");
   if (plan->kind != TA_PLAN_VERIFY) return fail(TA_ERR_STATE, "accept_scratch_bytes: needs a verify plan");
   if (vocab < 1 || vocab > INT32_MAX) return fail(TA_ERR_INVALID_ARG, "accept_scratch_bytes: vocab must be in [1, 2^31)");
@@ -414,11 +435,13 @@ extern "C" int tree_attn_accept_scratch_bytes(const ta_plan* plan, int64_t vocab
   accept_geometry(rows, vocab, &chunks, &ce);
   *bytes = size_t(2 * align256(rows * chunks * 4));
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("accept_scratch_bytes");
 }
 
 extern "C" int tree_attn_accept(const ta_plan* plan, int32_t dtype, const void* logits, int64_t vocab, int64_t ld,
                                 const int32_t* tokens, double tau, int32_t mode, int32_t* path, int32_t* n_path,
-                                int32_t* next_token, void* scratch, size_t scratch_bytes, void* stream) {
+                                int32_t* next_token, void* scratch, size_t scratch_bytes, void* stream) try {
   int rc = check_plan(plan, TA_PLAN_VERIFY, "accept");
   if (rc) return rc;
   if (dtype != TA_DTYPE_BF16 && dtype != TA_DTYPE_F32)
@@ -466,4 +489,6 @@ extern "C" int tree_attn_accept(const ta_plan* plan, int32_t dtype, const void* 
   p.n_path = n_path;
   p.next_token = next_token;
   return hip_status(launch_accept(dtype, p, rows, static_cast<hipStream_t>(stream)), "accept launch");
+} catch (...) {
+  return ta::fail_exception("accept");
 }

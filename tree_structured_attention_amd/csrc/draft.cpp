@@ -48,7 +48,7 @@ struct Trie {
 extern "C" int tree_attn_draft_tree(const int32_t* accepted, int32_t n_accepted, const int32_t* drafts,
                                     const int32_t* draft_len, int32_t n_drafts, int32_t window,
                                     int32_t max_nodes, int32_t max_depth, int32_t* tokens, int32_t* parent,
-                                    int32_t* n_nodes) {
+                                    int32_t* n_nodes) try {
   if (!n_nodes) return fail(TA_ERR_INVALID_ARG, "draft_tree: n_nodes is NULL");
   if (n_accepted < 0 || n_drafts < 0) return fail(TA_ERR_INVALID_ARG, "draft_tree: negative count");
   if (window < 1) return fail(TA_ERR_INVALID_ARG, "draft_tree: window must be >= 1");
@@ -97,4 +97,6 @@ extern "C" int tree_attn_draft_tree(const int32_t* accepted, int32_t n_accepted,
   }
   *n_nodes = int32_t(n);
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("draft_tree");
 }

@@ -12,6 +12,7 @@
 // own table (segment B), so a partially filled shared block is never written
 // by the fork and needs no copy.
 #include <algorithm>
+#include <memory>
 #include <climits>
 #include <set>
 #include <vector>
@@ -37,22 +38,25 @@ struct ta_kv_pool {
   }
 };
 
-extern "C" int tree_attn_pool_create(int32_t n_blocks, int32_t block_size, ta_kv_pool** out) {
+extern "C" int tree_attn_pool_create(int32_t n_blocks, int32_t block_size, ta_kv_pool** out) try {
   if (!out) return fail(TA_ERR_INVALID_ARG, "pool_create: out is NULL");
   if (n_blocks < 0 || block_size < 1) return fail(TA_ERR_INVALID_ARG, "pool_create: bad size");
   if (int64_t(n_blocks) * block_size >= INT32_MAX) return fail(TA_ERR_CAPACITY, "pool_create: token rows >= 2^31");
-  auto* p = new ta_kv_pool();
+  std::unique_ptr<ta_kv_pool> owner(new ta_kv_pool());
+  ta_kv_pool* p = owner.get();
   p->n_blocks = n_blocks;
   p->block_size = block_size;
   p->ref.assign(size_t(n_blocks), 0);
   for (int32_t b = 0; b < n_blocks; ++b) p->free_set.insert(p->free_set.end(), b);
-  *out = p;
+  *out = owner.release();
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("pool_create");
 }
 
 extern "C" void tree_attn_pool_destroy(ta_kv_pool* pool) { delete pool; }
 
-extern "C" int tree_attn_pool_new_seq(ta_kv_pool* pool, int32_t* seq) {
+extern "C" int tree_attn_pool_new_seq(ta_kv_pool* pool, int32_t* seq) try {
   if (!pool || !seq) return fail(TA_ERR_INVALID_ARG, "pool_new_seq: NULL argument");
   if (pool->seqs.size() >= size_t(INT32_MAX)) return fail(TA_ERR_CAPACITY, "pool_new_seq: sequence ids exhausted");
   ta_kv_pool::Seq s;
@@ -61,9 +65,11 @@ extern "C" int tree_attn_pool_new_seq(ta_kv_pool* pool, int32_t* seq) {
   pool->seqs.push_back(std::move(s));
   *seq = int32_t(pool->seqs.size() - 1);
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("pool_new_seq");
 }
 
-extern "C" int tree_attn_pool_fork(ta_kv_pool* pool, int32_t parent, int32_t n_tokens, int32_t* child) {
+extern "C" int tree_attn_pool_fork(ta_kv_pool* pool, int32_t parent, int32_t n_tokens, int32_t* child) try {
   if (!pool || !child) return fail(TA_ERR_INVALID_ARG, "pool_fork: NULL argument");
   const ta_kv_pool::Seq* p = pool->get(parent);
   if (!p || !p->root) return fail(TA_ERR_INVALID_ARG, "pool_fork: the parent must be a live root sequence");
@@ -79,9 +85,11 @@ extern "C" int tree_attn_pool_fork(ta_kv_pool* pool, int32_t parent, int32_t n_t
   pool->seqs.push_back(std::move(s));
   *child = int32_t(pool->seqs.size() - 1);
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("pool_fork");
 }
 
-extern "C" int tree_attn_pool_append(ta_kv_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots) {
+extern "C" int tree_attn_pool_append(ta_kv_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots) try {
   if (!pool) return fail(TA_ERR_INVALID_ARG, "pool_append: pool is NULL");
   ta_kv_pool::Seq* s = pool->get(seq);
   if (!s) return fail(TA_ERR_INVALID_ARG, "pool_append: unknown sequence");
@@ -101,9 +109,11 @@ extern "C" int tree_attn_pool_append(ta_kv_pool* pool, int32_t seq, int32_t n_to
   for (int64_t t = s->own_len; t < new_len; ++t) slots[t - s->own_len] = int64_t(s->own[t / bs]) * bs + t % bs;
   s->own_len = new_len;
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("pool_append");
 }
 
-extern "C" int tree_attn_pool_release(ta_kv_pool* pool, int32_t seq) {
+extern "C" int tree_attn_pool_release(ta_kv_pool* pool, int32_t seq) try {
   if (!pool) return fail(TA_ERR_INVALID_ARG, "pool_release: pool is NULL");
   ta_kv_pool::Seq* s = pool->get(seq);
   if (!s) return fail(TA_ERR_INVALID_ARG, "pool_release: unknown sequence");
@@ -116,10 +126,12 @@ extern "C" int tree_attn_pool_release(ta_kv_pool* pool, int32_t seq) {
   s->view.shrink_to_fit();
   s->own.shrink_to_fit();
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("pool_release");
 }
 
 extern "C" int tree_attn_pool_table(const ta_kv_pool* pool, int32_t seq, int32_t* view, int32_t view_cap,
-                                    int32_t* view_tokens, int32_t* own, int32_t own_cap, int32_t* own_tokens) {
+                                    int32_t* view_tokens, int32_t* own, int32_t own_cap, int32_t* own_tokens) try {
   if (!pool || !view_tokens || !own_tokens) return fail(TA_ERR_INVALID_ARG, "pool_table: NULL argument");
   if (seq < 0 || size_t(seq) >= pool->seqs.size() || !pool->seqs[seq].live)
     return fail(TA_ERR_INVALID_ARG, "pool_table: unknown sequence");
@@ -132,9 +144,11 @@ extern "C" int tree_attn_pool_table(const ta_kv_pool* pool, int32_t seq, int32_t
   std::copy(s.view.begin(), s.view.end(), view);
   std::copy(s.own.begin(), s.own.end(), own);
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("pool_table");
 }
 
-extern "C" int tree_attn_pool_refs(const ta_kv_pool* pool, int32_t* refs, int32_t cap, int32_t* free_blocks) {
+extern "C" int tree_attn_pool_refs(const ta_kv_pool* pool, int32_t* refs, int32_t cap, int32_t* free_blocks) try {
   if (!pool || !free_blocks) return fail(TA_ERR_INVALID_ARG, "pool_refs: NULL argument");
   *free_blocks = int32_t(pool->free_set.size());
   if (refs) {
@@ -142,4 +156,6 @@ extern "C" int tree_attn_pool_refs(const ta_kv_pool* pool, int32_t* refs, int32_
     std::copy(pool->ref.begin(), pool->ref.end(), refs);
   }
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("pool_refs");
 }

@@ -14,6 +14,7 @@
 // at most two contiguous intervals, so no mask memory is needed outside the
 // 64-node draft trees.
 #include <algorithm>
+#include <memory>
 #include <climits>
 #include <cstring>
 #include <numeric>
@@ -127,10 +128,11 @@ void pack_blob(ta_plan* p) {
   L.tile_b = off;
   off = align256(off + int64_t(p->tile_b.size() * 4));
   L.total = std::max<int64_t>(off, 256);
-  p->layout = L;
-  p->blob.assign(size_t(L.total), 0);
+  // the image is built aside and swapped in, so a failed allocation leaves
+  // the plan as it was
+  std::vector<unsigned char> blob(size_t(L.total), 0);
   auto put = [&](int64_t at, const void* src, size_t n) {
-    if (n) std::memcpy(p->blob.data() + at, src, n);
+    if (n) std::memcpy(blob.data() + at, src, n);
   };
   put(L.work, p->work.data(), p->work.size() * sizeof(WorkItem));
   put(L.row_a, p->row_a.data(), p->row_a.size() * 4);
@@ -142,6 +144,8 @@ void pack_blob(ta_plan* p) {
   put(L.trees, p->tree_tab.data(), p->tree_tab.size() * 4);
   put(L.tile_a, p->tile_a.data(), p->tile_a.size() * 4);
   put(L.tile_b, p->tile_b.data(), p->tile_b.size() * 4);
+  p->blob.swap(blob);
+  p->layout = L;
 }
 
 }  // namespace ta
@@ -150,7 +154,7 @@ using namespace ta;
 
 extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* n_regions,
                                       const int32_t* layout_len, const int32_t* content_len,
-                                      int32_t n_pages, ta_plan** out) {
+                                      int32_t n_pages, ta_plan** out) try {
   if (!out) return fail(TA_ERR_INVALID_ARG, "plan_prefill: out is NULL");
   if (n_pages < 0) return fail(TA_ERR_INVALID_ARG, "plan_prefill: n_pages < 0");
   if (n_pages > 0 && (!prefix_len || !n_regions))
@@ -176,7 +180,9 @@ extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* 
     }
   }
 
-  auto* pl = new ta_plan();
+  // owned here until handed out, so a throwing resize cannot leak it
+  std::unique_ptr<ta_plan> owner(new ta_plan());
+  ta_plan* pl = owner.get();
   pl->kind = TA_PLAN_PREFILL;
   pl->n_pages = n_pages;
   pl->n_branches = int32_t(total_regions);
@@ -311,8 +317,10 @@ extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* 
   }
   order_work(pl->work);
   pack_blob(pl);
-  *out = pl;
+  *out = owner.release();
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("plan_prefill");
 }
 
 namespace {
@@ -371,7 +379,9 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
     if (rc) return rc;
   }
 
-  auto* pl = new ta_plan();
+  // owned here until handed out, so a throwing resize cannot leak it
+  std::unique_ptr<ta_plan> owner(new ta_plan());
+  ta_plan* pl = owner.get();
   pl->kind = TA_PLAN_DECODE;
   pl->n_pages = n_pages;
   pl->n_branches = n_branches;
@@ -497,13 +507,12 @@ int build_decode(const int32_t* prefix_len, const int32_t* n_regions, const int3
     }
   }
   if (slot >= kMax32) {
-    delete pl;
     return fail(TA_ERR_CAPACITY, "plan_decode: partial slots >= 2^31");
   }
   pl->n_partials = slot;
   order_work(pl->work);
   pack_blob(pl);
-  *out = pl;
+  *out = owner.release();
   return TA_OK;
 }
 
@@ -513,19 +522,23 @@ extern "C" int tree_attn_plan_decode(const int32_t* prefix_len, const int32_t* n
                                      const int32_t* layout_len, int32_t n_pages,
                                      const int32_t* br_page, const int32_t* br_region,
                                      const int32_t* suffix_len, int32_t n_branches,
-                                     ta_plan** out) {
+                                     ta_plan** out) try {
   return build_decode(prefix_len, n_regions, layout_len, n_pages, br_page, br_region, suffix_len, nullptr,
                       n_branches, Paging{}, Paging{}, out);
+} catch (...) {
+  return ta::fail_exception("plan_decode");
 }
 
 extern "C" int tree_attn_plan_decode_multi(const int32_t* prefix_len, const int32_t* n_regions,
                                            const int32_t* layout_len, int32_t n_pages,
                                            const int32_t* br_page, const int32_t* br_region,
                                            const int32_t* suffix_len, const int32_t* n_query,
-                                           int32_t n_branches, ta_plan** out) {
+                                           int32_t n_branches, ta_plan** out) try {
   if (n_branches > 0 && !n_query) return fail(TA_ERR_INVALID_ARG, "plan_decode_multi: NULL n_query");
   return build_decode(prefix_len, n_regions, layout_len, n_pages, br_page, br_region, suffix_len, n_query,
                       n_branches, Paging{}, Paging{}, out);
+} catch (...) {
+  return ta::fail_exception("plan_decode_multi");
 }
 
 extern "C" int tree_attn_plan_decode_paged(const int32_t* prefix_len, const int32_t* n_regions,
@@ -535,7 +548,7 @@ extern "C" int tree_attn_plan_decode_paged(const int32_t* prefix_len, const int3
                                            int32_t n_branches, int32_t block_size, int32_t n_cache_blocks,
                                            const int32_t* main_blocks, const int64_t* main_block_off,
                                            const int32_t* suffix_blocks, const int64_t* suffix_block_off,
-                                           ta_plan** out) {
+                                           ta_plan** out) try {
   Paging pa, pb;
   pa.bs = pb.bs = block_size;
   pa.n_cache_blocks = pb.n_cache_blocks = n_cache_blocks;
@@ -546,6 +559,8 @@ extern "C" int tree_attn_plan_decode_paged(const int32_t* prefix_len, const int3
   if (block_size <= 0) return fail(TA_ERR_INVALID_ARG, "plan_decode_paged: block_size must be a positive multiple of 64");
   return build_decode(prefix_len, n_regions, layout_len, n_pages, br_page, br_region, suffix_len, n_query,
                       n_branches, pa, pb, out);
+} catch (...) {
+  return ta::fail_exception("plan_decode_paged");
 }
 
 namespace {
@@ -594,7 +609,9 @@ int build_verify(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page
     if (rc) return rc;
   }
 
-  auto* pl = new ta_plan();
+  // owned here until handed out, so a throwing resize cannot leak it
+  std::unique_ptr<ta_plan> owner(new ta_plan());
+  ta_plan* pl = owner.get();
   pl->kind = TA_PLAN_VERIFY;
   pl->n_pages = n_pages;
   pl->n_branches = n_branches;
@@ -645,7 +662,7 @@ int build_verify(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page
   }
   order_work(pl->work);
   pack_blob(pl);
-  *out = pl;
+  *out = owner.release();
   return TA_OK;
 }
 
@@ -653,14 +670,16 @@ int build_verify(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page
 
 extern "C" int tree_attn_plan_verify(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page,
                                      const int32_t* n_nodes, const int32_t* parent, int32_t n_branches,
-                                     ta_plan** out) {
+                                     ta_plan** out) try {
   return build_verify(ctx_len, n_pages, br_page, n_nodes, parent, n_branches, Paging{}, out);
+} catch (...) {
+  return ta::fail_exception("plan_verify");
 }
 
 extern "C" int tree_attn_plan_verify_paged(const int32_t* ctx_len, int32_t n_pages, const int32_t* br_page,
                                            const int32_t* n_nodes, const int32_t* parent, int32_t n_branches,
                                            int32_t block_size, int32_t n_cache_blocks, const int32_t* ctx_blocks,
-                                           const int64_t* ctx_block_off, ta_plan** out) {
+                                           const int64_t* ctx_block_off, ta_plan** out) try {
   Paging pa;
   pa.bs = block_size;
   pa.n_cache_blocks = n_cache_blocks;
@@ -668,6 +687,8 @@ extern "C" int tree_attn_plan_verify_paged(const int32_t* ctx_len, int32_t n_pag
   pa.off = ctx_block_off;
   if (block_size <= 0) return fail(TA_ERR_INVALID_ARG, "plan_verify_paged: block_size must be a positive multiple of 64");
   return build_verify(ctx_len, n_pages, br_page, n_nodes, parent, n_branches, pa, out);
+} catch (...) {
+  return ta::fail_exception("plan_verify_paged");
 }
 
 namespace {
@@ -691,7 +712,7 @@ constexpr int64_t kItemOverhead = 3;  // prologue/epilogue of a workgroup, in ti
 
 }  // namespace
 
-extern "C" int tree_attn_plan_balance(ta_plan* plan, int32_t n_kv_heads, int32_t n_slots) {
+extern "C" int tree_attn_plan_balance(ta_plan* plan, int32_t n_kv_heads, int32_t n_slots) try {
   if (!plan) return fail(TA_ERR_INVALID_ARG, "plan_balance: plan is NULL");
   if (n_kv_heads <= 0 || n_slots <= 0) return fail(TA_ERR_INVALID_ARG, "plan_balance: counts must be positive");
   if (plan->kind == TA_PLAN_DECODE) return TA_OK;  // decode items are already key chunks
@@ -767,7 +788,17 @@ extern "C" int tree_attn_plan_balance(ta_plan* plan, int32_t n_kv_heads, int32_t
   order_work(out);
   plan->work.swap(out);
   plan->merge.swap(merge);
+  const int64_t old_partials = plan->n_partials;
   plan->n_partials = slot;
-  pack_blob(plan);
+  try {
+    pack_blob(plan);
+  } catch (...) {  // a failed balance leaves the plan unbalanced and usable
+    plan->work.swap(out);
+    plan->merge.swap(merge);
+    plan->n_partials = old_partials;
+    throw;
+  }
   return TA_OK;
+} catch (...) {
+  return ta::fail_exception("plan_balance");
 }

@@ -130,5 +130,6 @@ namespace ta {
 int64_t item_tiles(const WorkItem& w);
 void set_error(const std::string& msg);
 int fail(int code, const std::string& msg);
+int fail_exception(const char* who) noexcept;
 void pack_blob(ta_plan* p);
 }  // namespace ta
