@@ -4,21 +4,29 @@
 
 One step is one pass of every forward entry point over resident synthetic
 inputs:
-  prefill  one packed page: P = 4096, 24 regions of 12 layout tokens,
-           lognormal content (8,772 tokens), 16q/8kv heads, d = 128, bf16
+  prefill  the packed batch of eight pages: P = 4096, N ~ U{12..40} regions
+           of 12 layout tokens, lognormal content, 77,400 tokens (seed 2),
+           16q/8kv heads, d = 128, bf16 -- the headline `value`
   decode   16 pages x 24 live branches, P = 4809, s_k ~ U{0..1024}
   verify   64 pages x 8 draft trees of 32 nodes, contexts ~ U{4096..16384}
-The prefill backward (dq, dk, dv of the same page), the greedy acceptance
-walk over the verify trees (bf16 logits, 151,936-entry vocabulary) and a
-multi-token decode (8-token windows for the decode pages' 24 branches plus
-one layout-stream row per page) and the decode workload read from a paged
-cache of 64-token blocks are timed in the same loop and reported under
-entries, outside the step.
+           shared by the trees of a page
+Timed in the same loop and reported under `entries`, outside the step: the
+one-page prefill (8,772 tokens, seed 1), verify with 512 independent
+prefixes (one tree per context), the prefill backward (dq, dk, dv of the
+one-page workload), the greedy acceptance walk over the verify trees (bf16
+logits, 151,936-entry vocabulary), a multi-token decode (8-token windows for
+the decode pages' 24 branches plus one layout-stream row per page) and the
+decode workload read from a paged cache of 64-token blocks.
+
 Each entry point is bracketed by HIP events on the stream it is launched on
-(torch's current stream).  The single JSON line on stdout reports prefill
-packed tokens/s as `value`, with decode and verify beside it, a roofline per
-kernel (algorithmic FLOPs or bytes per launch over the measured average
-launch time) and the fp64 CPU oracle timed on a bounded sample.
+(torch's current stream).  Every entry reports both roofline components --
+algorithmic FLOPs (4 d Hq per visible pair; 8 d Hq in the backward) and
+algorithmic bytes (every distinct input byte read once, every output byte
+written once) over the average launch time -- against MI355X's published
+peaks (2.5 PFLOP/s dense bf16, 8 TB/s) and against the peaks two
+calibration loops reach on this GPU (an MFMA loop and a streaming read).
+The fp64 CPU oracle is timed on bounded samples of the prefill, decode and
+verify workloads on this host's cores.  One JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -56,9 +64,12 @@ def scratch_for(plan, w):
     return torch.empty(n + 256, dtype=torch.uint8, device="cuda") if n else None
 
 
-def prefill_case():
-    w = synth.config2()
-    ta.plan_for(w.desc).balance(w.hkv)  # the host plan's steady-state cost is timed below
+def prefill_case(w=None, name="prefill", in_step=True):
+    """Packed prefill over a balanced plan (row tiles split so the launch
+    fills the chip); the host plan's steady-state cost is timed on a second
+    build."""
+    w = w or synth.config3()
+    ta.plan_for(w.desc).balance(w.hkv)
     t0 = time.perf_counter()
     plan = ta.plan_for(w.desc).balance(w.hkv)
     plan_us = (time.perf_counter() - t0) * 1e6
@@ -72,9 +83,19 @@ def prefill_case():
     def run():
         ta.prefill(plan, t["q"], t["k"], t["v"], scale=w.scale, out=o, lse=lse, scratch=scratch)
 
+    e = elt(w.dtype)
+    rows = info["n_rows"]
+    # q, k, v read once, o and lse written once
+    bytes_ = rows * (2 * w.hq + 2 * w.hkv) * w.head_dim * e + rows * w.hq * 4
     flops = 4.0 * w.head_dim * w.hq * info["visible_pairs"]
-    return dict(name="prefill", w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="packed tokens",
-                flops=flops, bytes=None, bound="mfma", plan_us=plan_us, kernel="attn_kernel<bf16,128,2,prefill> (+ merge_kernel for split tiles)")
+    return dict(name=name, w=w, plan=plan, run=run, unit_count=rows, unit="packed tokens", flops=flops,
+                bytes=bytes_, bound="mfma", plan_us=plan_us, in_step=in_step,
+                kernel="attn_kernel<bf16,128,2,prefill> (+ merge_kernel for split tiles)")
+
+
+def prefill_1page_case():
+    """The one-page prefill (P = 4096, 24 regions, 8,772 tokens)."""
+    return prefill_case(synth.config2(), "prefill_1page", in_step=False)
 
 
 def decode_case(w=None, name="decode"):
@@ -175,14 +196,14 @@ def decode_multi_case():
     return decode_case(synth.decode_multi(), "decode_multi")
 
 
-def verify_case():
-    w = synth.config5()
+def verify_case(w=None, name="verify", in_step=True, tensors=None):
+    w = w or synth.config5()
     ta.plan_for(w.desc).balance(w.hkv)
     t0 = time.perf_counter()
     plan = ta.plan_for(w.desc).balance(w.hkv)
     plan_us = (time.perf_counter() - t0) * 1e6
     plan.upload()
-    t = {k: v.cuda() for k, v in w.tensors.items()}
+    t = tensors if tensors is not None else {k: v.cuda() for k, v in w.tensors.items()}
     o = torch.empty_like(t["q"])
     lse = torch.empty((w.hq, t["q"].shape[0]), dtype=torch.float32, device="cuda")
     scratch = scratch_for(plan, w)
@@ -195,9 +216,20 @@ def verify_case():
     e = elt(w.dtype)
     flops = 4.0 * w.head_dim * w.hq * info["visible_pairs"]
     bytes_ = ((info["n_keys_a"] + info["n_keys_b"]) * w.hkv * w.head_dim * 2 * e
-              + info["n_rows"] * w.hq * w.head_dim * 2 * e)
-    return dict(name="verify", w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="draft nodes",
-                flops=flops, bytes=bytes_, bound="mfma", plan_us=plan_us, kernel="attn_kernel<bf16,128,2,verify>")
+              + info["n_rows"] * w.hq * w.head_dim * 2 * e + info["n_rows"] * w.hq * 4)
+    bound = "mfma" if flops / (PEAK_BF16_TFLOPS * 1e12) >= bytes_ / (PEAK_HBM_GBS * 1e9) else "hbm"
+    return dict(name=name, w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="draft nodes",
+                flops=flops, bytes=bytes_, bound=bound, plan_us=plan_us, in_step=in_step,
+                kernel="attn_kernel<bf16,128,2,verify> (+ merge_kernel for split tiles)")
+
+
+def verify_unshared_case():
+    """The 512 draft trees of the verify workload, each over a prefix of its
+    own (512 contexts ~ U{4096..16384}, 21.7 GB of K/V): the HBM-bound
+    reading of the verify workload.  Inputs drawn on the GPU."""
+    w = synth.config5_unshared()
+    t = synth.verify_tensors_device(41, w.desc, w.hq, w.hkv, w.head_dim, w.dtype)
+    return verify_case(w, "verify_unshared", in_step=False, tensors=t)
 
 
 def backward_case():
@@ -222,8 +254,11 @@ def backward_case():
     # dv = P^T dO, dP = dO V^T, dq = dS K, dk = dS^T Q: 4 products of 2 d flops
     # per visible pair and query head (the recomputed S is not counted)
     flops = 8.0 * w.head_dim * w.hq * info["visible_pairs"]
-    return dict(name="backward", w=w, plan=plan, run=run, unit_count=info["n_rows"], unit="packed tokens",
-                flops=flops, bytes=None, bound="mfma", plan_us=0.0, in_step=False,
+    # q, o, dO (Hq heads), k, v (Hkv) and lse read once; dq, dk, dv written once
+    rows = info["n_rows"]
+    bytes_ = rows * (4 * w.hq + 4 * w.hkv) * w.head_dim * 2 + rows * w.hq * 4
+    return dict(name="backward", w=w, plan=plan, run=run, unit_count=rows, unit="packed tokens",
+                flops=flops, bytes=bytes_, bound="mfma", plan_us=0.0, in_step=False,
                 kernel="bwd_prep_kernel<128> + bwd_dq_kernel<128,2> + bwd_dkdv_kernel<128>")
 
 
@@ -287,36 +322,146 @@ def traffic_for(entry):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(budget_s: float):
-    """The fp64 oracle on a bounded, evenly spread sample of the prefill rows."""
-    import oracle  # test infrastructure: used only for this reported baseline
+def host_cpu():
+    """The host's cores as the oracle sees them: os.cpu_count(), the cores
+    this process may run on, the BLAS thread count and the CPU model."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    w = synth.config2()
-    P = int(w.desc.prefix_len[0])
-    L = w.desc.layout_len
-    C = w.desc.content_len
-    T = w.desc.total_tokens()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"cpu_count": os.cpu_count(), "usable_cores": affinity, "blas_threads": int(threads), "cpu_model": model}
+
+
+def _baseline(done, elapsed, unit, cpu, sample):
+    return {"value": done / elapsed, "unit": unit, "cores": cpu["blas_threads"], "kind": "oracle",
+            "sample": sample, "seconds": elapsed, **cpu}
+
+
+def cpu_prefill(w, budget_s, cpu):
+    """The fp64 oracle on the packed prefill batch: pages in a random order,
+    each page's dense ancestor mask built (and timed), then its rows in a
+    random order in blocks of 256, until the budget is spent."""
+    import oracle  # test infrastructure: used only for this reported baseline
+    desc, t = w.desc, w.tensors
+    rng = np.random.default_rng(0)
+    reg = np.concatenate([[0], np.cumsum(desc.n_regions.astype(np.int64))])
+    tok = np.concatenate([[0], np.cumsum(desc.page_tokens())])
+    done, pages_seen = 0, 0
     t0 = time.perf_counter()
-    mask = oracle.ancestor_mask_page(P, L, C)
-    order = np.random.default_rng(0).permutation(T)
-    done = 0
-    block = 256
-    # rows in a fixed random order, cycling through the page until the budget
-    # is spent (a fast host finishes one pass well inside it)
     while time.perf_counter() - t0 < budget_s:
-        start = done % T
-        rows = np.sort(order[start:min(T, start + block)])
-        oracle.masked_attention(w.tensors["q"][rows], w.tensors["k"], w.tensors["v"], mask[rows], w.scale)
+        for p in rng.permutation(desc.n_pages):
+            L = desc.layout_len[reg[p]:reg[p + 1]]
+            C = desc.content_len[reg[p]:reg[p + 1]]
+            base, T = int(tok[p]), int(tok[p + 1] - tok[p])
+            mask = oracle.ancestor_mask_page(int(desc.prefix_len[p]), L, C)
+            pages_seen += 1
+            order = rng.permutation(T)
+            for i in range(0, T, 256):
+                rows = np.sort(order[i:i + 256])
+                oracle.masked_attention(t["q"][base + rows], t["k"][base:base + T], t["v"][base:base + T],
+                                        mask[rows], w.scale)
+                done += len(rows)
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    el = time.perf_counter() - t0
+    return _baseline(done, el, "packed tokens/s", cpu,
+                     f"{done} rows of the {desc.total_tokens()}-token {desc.n_pages}-page prefill batch "
+                     f"({pages_seen} page masks built), random rows in blocks of 256, all {w.hq} heads, fp64 numpy "
+                     f"with the dense ancestor mask, {el:.1f} s")
+
+
+def cpu_decode(w, budget_s, cpu):
+    """The fp64 decode oracle on rows in a random order, 16 at a time."""
+    import oracle
+    t = w.tensors
+    n = w.desc.n_rows()
+    order = np.random.default_rng(0).permutation(n)
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        start = done % n
+        rows = order[start:min(n, start + 16)]
+        oracle.decode(w.desc, t["q"], t["k_main"], t["v_main"], t["k_suffix"], t["v_suffix"], w.scale, rows=rows)
         done += len(rows)
     el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "packed tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} row evaluations over the {T} rows of the one-page prefill workload ({done / T:.2f} "
-                      f"passes; random row order, all 16 heads, fp64 numpy with the dense ancestor mask), "
-                      f"{el:.1f} s"}
+    return _baseline(done, el, "query tokens/s", cpu,
+                     f"{done} of the {n} branch rows (16 per call, random order), all {w.hq} heads, fp64 numpy, "
+                     f"{el:.1f} s")
+
+
+def cpu_verify(w, budget_s, cpu):
+    """The fp64 verify oracle page by page (a page's 8 trees together, its
+    context and tree mask explicit), pages in a random order."""
+    import oracle
+    t = w.tensors
+    desc = w.desc
+    per_page = np.bincount(desc.br_page, weights=desc.n_nodes, minlength=desc.n_pages).astype(np.int64)
+    done, pages = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        for p in np.random.default_rng(pages).permutation(desc.n_pages):
+            oracle.verify(desc, t["q"], t["k_ctx"], t["v_ctx"], t["k_tree"], t["v_tree"], w.scale, pages=[int(p)])
+            done += int(per_page[p])
+            pages += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    el = time.perf_counter() - t0
+    return _baseline(done, el, "draft nodes/s", cpu,
+                     f"{pages} of the {desc.n_pages} pages ({done} draft nodes), all {w.hq} heads, fp64 numpy with "
+                     f"the explicit tree mask, {el:.1f} s")
+
+
+def calibrate():
+    """Attainable peaks on this GPU: the best rate of the MFMA loop and of
+    the streaming read over a few launch shapes, three launches each."""
+    def timed(fn, reps=3):
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            work = fn()
+            b.record()
+            torch.cuda.synchronize()
+            sec = a.elapsed_time(b) / 1e3
+            best = work / sec if best is None else max(best, work / sec)
+        return best
+
+    sink = torch.empty(4 * 4096, dtype=torch.float32, device="cuda")
+    mfma = {blocks: timed(lambda: ta.calib_mfma(blocks, 4000, sink)) / 1e12 for blocks in (1024, 2048, 4096)}
+    src = torch.ones(1 << 32, dtype=torch.uint8, device="cuda")  # 4 GiB
+    rsink = torch.empty(32768, dtype=torch.int32, device="cuda")
+    read = {blocks: timed(lambda: ta.calib_read(src, blocks, rsink)) / 1e9 for blocks in (2048, 4096, 8192, 16384, 32768)}
+    del src
+    return {"mfma_bf16_tflops": max(mfma.values()), "hbm_read_gbs": max(read.values()),
+            "mfma_loop": "tree_attn_calib_mfma: waves issuing back-to-back bf16 32x32x16 MFMAs on 8 accumulators, "
+                         "4,000 rounds; best of 1024/2048/4096 workgroups of 4 waves: "
+                         + ", ".join(f"{k}: {v:.0f}" for k, v in mfma.items()) + " TFLOP/s",
+            "read_loop": "tree_attn_calib_read: 4 GiB streamed with 16-byte non-temporal loads; best of "
+                         "2048-32768 workgroups of 256 threads: "
+                         + ", ".join(f"{k}: {v:.0f}" for k, v in read.items()) + " GB/s"}
+
+
+ENTRIES = {
+    "prefill": prefill_case, "decode": decode_case, "verify": verify_case, "prefill_1page": prefill_1page_case,
+    "verify_unshared": verify_unshared_case, "backward": backward_case, "accept": accept_case,
+    "decode_multi": decode_multi_case, "decode_paged": decode_paged_case,
+}
 
 
 def main():
@@ -324,11 +469,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for each CPU baseline (prefill, decode, verify)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward", "accept", "decode_multi",
-                                       "decode_paged"],
-                    default=None,
+    ap.add_argument("--no-calib", action="store_true", help="skip the attainable-peak loops")
+    ap.add_argument("--only", choices=sorted(ENTRIES), default=None,
                     help="time one entry point only (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB three times "
@@ -350,11 +495,14 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
         del src, dst
+    attainable = None
+    if not args.no_calib and args.only is None:
+        attainable = calibrate()
+        log(f"[bench] attainable: {attainable['mfma_bf16_tflops']:.0f} TFLOP/s bf16, "
+            f"{attainable['hbm_read_gbs']:.0f} GB/s read")
     log("[bench] generating inputs")
     cases = []
-    for name, fn in (("prefill", prefill_case), ("decode", decode_case), ("verify", verify_case),
-                     ("backward", backward_case), ("accept", accept_case), ("decode_multi", decode_multi_case),
-                     ("decode_paged", decode_paged_case)):
+    for name, fn in ENTRIES.items():
         if args.only is None or args.only == name:
             cases.append(fn())
             log(f"[bench] {name}: {cases[-1]['w'].name} ready")
@@ -383,21 +531,24 @@ def main():
         ms = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
         avg = float(np.mean(ms))
         sec = avg / 1e3
+        tflops = c["flops"] / sec / 1e12
+        gbs = c["bytes"] / sec / 1e9
         r = {"workload": c["w"].name, "kernel": c["kernel"], "ms_avg": avg, "ms_min": float(np.min(ms)),
              "ms_median": float(np.median(ms)), f"{c['unit'].replace(' ', '_')}_per_s": c["unit_count"] / sec,
-             "tflops": c["flops"] / sec / 1e12, "plan_build_us": c["plan_us"]}
+             "flops_per_launch": c["flops"], "bytes_per_launch": c["bytes"], "tflops": tflops, "gbs": gbs,
+             "flop_frac": tflops / PEAK_BF16_TFLOPS, "byte_frac": gbs / PEAK_HBM_GBS,
+             "plan_build_us": c["plan_us"]}
+        if attainable:
+            r["flop_frac_attainable"] = tflops / attainable["mfma_bf16_tflops"]
+            r["byte_frac_attainable"] = gbs / attainable["hbm_read_gbs"]
         if c["bound"] == "mfma":
-            ach = c["flops"] / sec / 1e12
-            r["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                             "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic_for(c["name"])}
+            r["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic_for(c["name"])}
         else:
-            ach = c["bytes"] / sec / 1e9
-            r["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                             "frac": ach / PEAK_HBM_GBS, "traffic": traffic_for(c["name"])}
-        if c["bytes"] is not None:
-            r["gbs"] = c["bytes"] / sec / 1e9
+            r["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": gbs / PEAK_HBM_GBS, "traffic": traffic_for(c["name"])}
         per_case[c["name"]] = r
-        log(f"[bench] {c['name']}: {avg * 1e3:.1f} us  {json.dumps(r['roofline'])}")
+        log(f"[bench] {c['name']}: {avg * 1e3:.1f} us  flop_frac={r['flop_frac']:.3f} byte_frac={r['byte_frac']:.3f}")
 
     step_names = [c["name"] for c in cases if c.get("in_step", True)] or [c["name"] for c in cases]
     step_ms = sum(per_case[n]["ms_avg"] for n in step_names)
@@ -417,30 +568,35 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "prefill 1 page P=4096 N=24 L=12 lognormal C (8,772 tokens) + decode 16 pages x 24 "
-                               "branches P=4809 + verify 64 pages x 8 trees x 32 nodes; 16q/8kv heads, d=128",
+        "config": {"workload": "packed tree-varlen prefill, batch of 8 pages (seed 2): P=4096, N~U{12..40} regions, "
+                               "L=12, lognormal content clipped to [8,1024], cap 16,384 per page, 77,400 packed "
+                               "tokens; 16q/8kv heads, d=128, bf16. Step also runs decode (16 pages x 24 branches, "
+                               "P=4809) and verify (64 pages x 8 trees x 32 nodes)",
                    "prefill_tokens": per_case.get("prefill", {}).get("workload"),
+                   "step_entries": step_names,
                    "parallelism": "single GPU"},
-        "roofline": dict(per_case[dominant]["roofline"], kernel=per_case[dominant]["kernel"]),
+        "roofline": dict(per_case[dominant]["roofline"], kernel=per_case[dominant]["kernel"], entry=dominant),
+        "attainable": attainable,
         "entries": per_case,
         "wall_ms_timed_region": wall * 1e3,
     }
+    for name, key in (("prefill", "prefill_mfma_frac"), ("prefill_1page", "prefill_1page_mfma_frac"),
+                      ("verify", "verify_mfma_frac"), ("verify_unshared", "verify_unshared_hbm_frac"),
+                      ("decode", "decode_hbm_frac"), ("backward", "backward_mfma_frac"),
+                      ("accept", "accept_hbm_frac"), ("decode_multi", "decode_multi_hbm_frac"),
+                      ("decode_paged", "decode_paged_hbm_frac")):
+        if name in per_case:
+            out[key] = per_case[name]["roofline"]["frac"]
     if "decode" in per_case:
         out["decode_query_tokens_per_s"] = per_case["decode"]["query_tokens_per_s"]
-        out["decode_hbm_frac"] = per_case["decode"]["roofline"]["frac"]
-    if "prefill" in per_case:
-        out["prefill_mfma_frac"] = per_case["prefill"]["roofline"]["frac"]
-    if "backward" in per_case:
-        out["backward_mfma_frac"] = per_case["backward"]["roofline"]["frac"]
-    if "accept" in per_case:
-        out["accept_hbm_frac"] = per_case["accept"]["roofline"]["frac"]
-    if "decode_multi" in per_case:
-        out["decode_multi_hbm_frac"] = per_case["decode_multi"]["roofline"]["frac"]
-    if "decode_paged" in per_case:
-        out["decode_paged_hbm_frac"] = per_case["decode_paged"]["roofline"]["frac"]
     if not args.no_cpu_baseline and args.only is None:
-        log("[bench] timing the CPU oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+        log("[bench] timing the CPU oracle baselines")
+        cpu = host_cpu()
+        byname = {c["name"]: c for c in cases}
+        per_case["prefill"]["cpu_baseline"] = cpu_prefill(byname["prefill"]["w"], args.cpu_budget, cpu)
+        per_case["decode"]["cpu_baseline"] = cpu_decode(byname["decode"]["w"], args.cpu_budget / 2, cpu)
+        per_case["verify"]["cpu_baseline"] = cpu_verify(byname["verify"]["w"], args.cpu_budget, cpu)
+        out["cpu_baseline"] = per_case["prefill"]["cpu_baseline"]
     print(json.dumps(out), flush=True)
 
 

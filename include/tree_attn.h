@@ -458,6 +458,26 @@ const char* tree_attn_last_error(void);
 /* Library version string. */
 const char* tree_attn_version(void);
 
+/* ---- Roofline calibration (measurement only; not part of the attention
+ * path).  Attention kernels are reported against MI355X's published peaks
+ * (2.5 PFLOP/s dense bf16, 8 TB/s HBM3E) and against what these two loops
+ * reach on the GPU at hand under load. */
+
+/* Enqueue `blocks` workgroups of 4 waves, each wave issuing `iters` rounds of
+ * 8 independent bf16 32x32x16 MFMAs from registers (no memory traffic in the
+ * loop).  *flops receives the launch's FLOP count (32,768 per MFMA); time
+ * the launch with events on `stream`.  sink: device, >= 4 * blocks floats
+ * (written, contents meaningless).  Errors: INVALID_ARG for blocks outside
+ * [1, 2^20], iters outside [1, 2^24] or a NULL / misaligned pointer. */
+int tree_attn_calib_mfma(int32_t blocks, int32_t iters, float* sink, int64_t* flops, void* stream);
+
+/* Enqueue a streaming read of `bytes` (a positive multiple of 16) at src
+ * (device, 16-byte aligned): `blocks` workgroups of 256 threads, 16-byte
+ * non-temporal loads, four in flight per thread, one word per workgroup
+ * written to sink (device, >= blocks uint32).  Errors: INVALID_ARG as for
+ * tree_attn_calib_mfma. */
+int tree_attn_calib_read(const void* src, int64_t bytes, int32_t blocks, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

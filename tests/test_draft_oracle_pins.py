@@ -61,6 +61,28 @@ def test_golden_draft_tree_round():
     assert path == ints(fx["path_exact"][0]) and free == int(fx["free_exact"][0][0])
 
 
+
+def oov_case():
+    fx = read_fixture("draft_tree_worked.txt")
+    V = int(fx["vocab"][0][0])
+    tok, par = ints(fx["oov_tokens"][0]), ints(fx["oov_parent"][0])
+    logp = np.full((len(tok) + 1, V), -10.0)
+    for r, t, s in fx["oov_score"]:
+        logp[int(r), int(t)] = float(s)
+    return fx, V, tok, par, logp
+
+
+def test_golden_out_of_vocabulary_tokens_are_never_accepted():
+    """A drafted token outside [0, V) (negative, or >= V) has no score, so
+    the walk skips its node; the hand-worked case puts the top score of a
+    row on the last column, where a negative token index would wrap."""
+    fx, V, tok, par, logp = oov_case()
+    path, free = oracle.tree_accept(tok, par, logp, float(fx["oov_tau"][0][0]))
+    assert path == ints(fx["oov_path"][0]) and free == int(fx["oov_free"][0][0])
+    path, free = oracle.tree_accept(tok, par, logp, exact=True)
+    assert path == ints(fx["oov_path_exact"][0]) and free == int(fx["oov_free_exact"][0][0])
+
+
 def _matches_by_bytes(w, d):
     """Match positions of w in d through bytes.find on a 4-byte encoding."""
     enc = lambda xs: b"".join(int(x).to_bytes(4, "little", signed=True) for x in xs)

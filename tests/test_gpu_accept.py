@@ -180,3 +180,32 @@ def test_accept_full_size_sampled():
         assert (path[lo:lo + n_path[b]].tolist(), int(nxt[b])) == want, b
         z_rows.append(z)
     del z_rows
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_out_of_vocabulary_tokens_golden(dtype):
+    """The hand-worked out-of-vocabulary case (tests/golden/
+    draft_tree_worked.txt): nodes whose drafted token is negative or >= V are
+    never taken, in tau and exact mode; paths and free tokens equal the
+    fixture's and the oracle's on the same stored logits."""
+    import os
+    gold = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "draft_tree_worked.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                key, *vals = line.split()
+                gold.setdefault(key, []).append(vals)
+    V = int(gold["vocab"][0][0])
+    tok = np.array([int(x) for x in gold["oov_tokens"][0]], np.int32)
+    par = np.array([int(x) for x in gold["oov_parent"][0]], np.int32)
+    z = np.full((len(tok) + 1, V), -10.0, np.float32)
+    for r, t, s in gold["oov_score"]:
+        z[int(r), int(t)] = float(s)
+    desc = synth.VerifyDesc(np.array([16], np.int32), np.zeros(1, np.int32), np.array([len(tok)], np.int32), par)
+    logits = torch.from_numpy(z).to(dtype).to(DEV)
+    for exact, pk, fk in ((False, "oov_path", "oov_free"), (True, "oov_path_exact", "oov_free_exact")):
+        path, n_path, nxt = run_accept(desc, tok, logits, V, float(gold["oov_tau"][0][0]), exact)
+        want = [int(x) for x in gold[pk][0]]
+        assert path[:n_path[0]].tolist() == want and int(nxt[0]) == int(gold[fk][0][0]), (exact, path, n_path, nxt)
+        check_against_oracle(desc, tok, logits, V, float(gold["oov_tau"][0][0]), exact)

@@ -134,10 +134,11 @@ def test_backward_config2_full_size_sampled():
     picks |= set(rng.integers(0, T, 12).tolist())
     idx = sorted(picks)
     rq, rk, rv = oracle.prefill_backward_sampled(desc, t["q"], t["k"], t["v"], g, w.scale, idx, idx)
-    # the tensors' scale is taken over the whole GPU result (the oracle only
-    # has the samples)
+    # each gradient's scale comes from the oracle: the largest magnitude over
+    # its samples, a lower bound of the tensor's max|ref|, so this is at least
+    # as strict as the per-tensor tolerance (no GPU value enters the bar)
     for got, ref, name in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
-        scale = float(np.abs(got).max())
+        scale = float(np.abs(ref).max())
         err = np.abs(got[idx] - ref)
         bad = err > 2e-2 * scale + 1e-2 * np.abs(ref)
         assert not bad.any(), f"{name}: {bad.sum()} outside; max_abs={err.max():.3g} scale={scale:.3g}"

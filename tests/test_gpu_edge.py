@@ -72,3 +72,25 @@ def test_verify_empty_and_single_node_trees_beside_full_ones():
         ro, rl = oracle.verify(w.desc, t["q"], t["k_ctx"], t["v_ctx"], t["k_tree"], t["v_tree"], w.scale)
         close(o, ro, TOL[w.dtype], f"verify edge trees heads={hq}/{hkv} o")
         close(lse, rl, LSE_TOL[w.dtype], f"verify edge trees heads={hq}/{hkv} lse")
+
+
+def test_calibration_loops_do_their_work():
+    """The roofline calibration loops: the streaming read folds every 4-byte
+    word of the buffer exactly once (the XOR over the workgroups' words
+    equals the buffer's XOR, for sizes with and without a ragged tail), and
+    the MFMA loop reports 32,768 FLOP per instruction."""
+    rng = np.random.default_rng(3)
+    for n_words in (1 << 20, (1 << 20) + 4 * 37):
+        words = rng.integers(-2**31, 2**31, n_words, dtype=np.int64).astype(np.int32)
+        src = torch.from_numpy(words).cuda()
+        sink = torch.zeros(300, dtype=torch.int32, device="cuda")
+        assert ta.calib_read(src, 300, sink) == 4 * n_words
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(words.view(np.uint32)), n_words
+    fsink = torch.zeros(4 * 8, dtype=torch.float32, device="cuda")
+    assert ta.calib_mfma(8, 10, fsink) == 8 * 4 * 10 * 8 * 32768
+    torch.cuda.synchronize()
+    assert torch.isfinite(fsink).all() and (fsink != 0).all()
+    with pytest.raises(ta.TreeAttnError):
+        ta.calib_read(src[:3], 4, sink)  # 12 bytes: not a multiple of 16

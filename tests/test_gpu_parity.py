@@ -474,3 +474,27 @@ def test_verify_score_range(kind):
     w.tensors["k_ctx"] = scale_keys(w.tensors["k_ctx"], kind)
     w.tensors["k_tree"] = scale_keys(w.tensors["k_tree"], kind)
     check_verify(w, tag=f"score range {kind}")
+
+
+def test_verify_unshared_full_size_sampled():
+    """Verify with 512 independent prefixes (one 32-node tree per context,
+    contexts ~ U{4096..16384}, 21.7 GB of K/V drawn on the GPU) in the launch
+    configuration the bench times (balanced plan); the trees of pages 0, 255
+    and 511 against the oracle."""
+    w = synth.config5_unshared()
+    t = synth.verify_tensors_device(41, w.desc, w.hq, w.hkv, w.head_dim, w.dtype)
+    plan = ta.plan_for(w.desc).balance(w.hkv).upload()
+    say(f"[verify] unshared: {w.desc.n_pages} contexts, {int(w.desc.ctx_len.sum())} context tokens")
+    o, lse = ta.verify(plan, t["q"], t["k_ctx"], t["v_ctx"], t["k_tree"], t["v_tree"], scale=w.scale)
+    torch.cuda.synchronize()
+    ctx_off = np.concatenate([[0], np.cumsum(w.desc.ctx_len.astype(np.int64))])
+    node_off = np.concatenate([[0], np.cumsum(w.desc.n_nodes.astype(np.int64))])
+    for p in (0, 255, 511):  # page p holds tree p
+        c0, c1, n0, n1 = int(ctx_off[p]), int(ctx_off[p + 1]), int(node_off[p]), int(node_off[p + 1])
+        sub = synth.VerifyDesc(w.desc.ctx_len[p:p + 1], np.zeros(1, np.int32), w.desc.n_nodes[p:p + 1],
+                               w.desc.parent[n0:n1])
+        ro, rl = oracle.verify(sub, t["q"][n0:n1].cpu(), t["k_ctx"][c0:c1].cpu(), t["v_ctx"][c0:c1].cpu(),
+                               t["k_tree"][n0:n1].cpu(), t["v_tree"][n0:n1].cpu(), w.scale)
+        e = close(o[n0:n1].float().cpu().numpy(), ro, TOL[w.dtype], f"unshared page {p} o")
+        close(lse[:, n0:n1].cpu().numpy(), rl, LSE_TOL[w.dtype], f"unshared page {p} lse")
+        say(f"    page {p}: ctx {c1 - c0}, max_abs o={e:.3g}")

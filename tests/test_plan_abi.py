@@ -15,7 +15,7 @@ from tree_structured_attention_amd import synth
 def test_library_exports_every_declared_symbol():
     L = ta.lib()
     declared = ta.header_symbols()
-    assert len(declared) == 30
+    assert len(declared) == 32
     for name in declared:
         assert hasattr(L, name), name
     assert L.tree_attn_version().decode().startswith("tree_attn")
@@ -461,3 +461,27 @@ def test_backward_scratch_checks_with_split_key_walks():
 
     assert call(need - 1) == ta.TA_ERR_WORKSPACE
     assert call(need) == ta.TA_ERR_STATE  # valid, but never uploaded
+
+
+@pytest.mark.parametrize("which", ["prefill", "prefill_balanced", "decode", "decode_multi", "verify"])
+def test_device_image_tables_equal_the_oracle_plan(which):
+    """The packed image that tree_attn_plan_upload copies holds, per row, the
+    bounds the oracle's plan defines, and the exported work list."""
+    import plan_image
+    if which.startswith("prefill"):
+        desc = synth.make_prefill_desc([200, 0, 65], [np.array([3, 0, 5, 2, 1]), np.array([4]), np.array([])],
+                                       [np.array([70, 0, 9, 130, 1]), np.array([3]), np.array([])])
+        plan = ta.plan_for(desc)
+        if which == "prefill_balanced":
+            plan.balance(8, 64)
+    elif which == "decode":
+        desc = synth.config4(with_tensors=False, n_pages=3).desc
+        plan = ta.plan_for(desc)
+    elif which == "decode_multi":
+        desc = synth.decode_multi(with_tensors=False, n_pages=2).desc
+        plan = ta.plan_for(desc)
+    else:
+        desc = synth.config5(with_tensors=False, n_pages=4).desc
+        plan = ta.plan_for(desc)
+    image = plan.export("device_image").view(np.uint8)
+    plan_image.check_against_oracle(plan, desc, image)

@@ -137,6 +137,8 @@ def lib() -> ctypes.CDLL:
             "tree_attn_accept_scratch_bytes": ([_P, i64, ctypes.POINTER(sz)], ctypes.c_int),
             "tree_attn_accept": ([_P, i32, _P, i64, i64, _P, ctypes.c_double, i32, _P, _P, _P, _P, sz, _P],
                                  ctypes.c_int),
+            "tree_attn_calib_mfma": ([i32, i32, _P, _I64P, _P], ctypes.c_int),
+            "tree_attn_calib_read": ([_P, i64, i32, _P, _P], ctypes.c_int),
             "tree_attn_last_error": ([], ctypes.c_char_p),
             "tree_attn_version": ([], ctypes.c_char_p),
         }
@@ -720,3 +722,28 @@ class KVPool:
             self.close()
         except Exception:
             pass
+
+
+# ---------------------------------------------------------------------------
+# roofline calibration (measurement only)
+# ---------------------------------------------------------------------------
+
+def calib_mfma(blocks: int, iters: int, sink: torch.Tensor, stream=None) -> int:
+    """Enqueue the bf16 MFMA loop; returns its FLOP count.  sink: float32
+    tensor of >= 4 * blocks entries on the GPU."""
+    if sink.dtype != torch.float32 or sink.numel() < 4 * blocks:
+        raise _bad("sink must be float32 with at least 4 * blocks entries")
+    flops = ctypes.c_int64()
+    _check(lib().tree_attn_calib_mfma(int(blocks), int(iters), _dev_ptr(sink), ctypes.byref(flops),
+                                      _stream_handle(stream)))
+    return int(flops.value)
+
+
+def calib_read(src: torch.Tensor, blocks: int, sink: torch.Tensor, stream=None) -> int:
+    """Enqueue the streaming read of the whole of src; returns its bytes.
+    sink: int32 tensor of >= blocks entries on the GPU."""
+    if sink.dtype != torch.int32 or sink.numel() < blocks:
+        raise _bad("sink must be int32 with at least `blocks` entries")
+    nbytes = src.numel() * src.element_size()
+    _check(lib().tree_attn_calib_read(_dev_ptr(src), nbytes, int(blocks), _dev_ptr(sink), _stream_handle(stream)))
+    return nbytes

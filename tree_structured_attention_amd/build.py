@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libtree_attn.so")
 
 ARCH = os.environ.get("TREE_ATTN_ARCH", "gfx950")
 HOST_SOURCES = ["plan.cpp", "api.cpp", "errors.cpp", "draft.cpp", "kv_pool.cpp"]
-HIP_SOURCES = ["attn_kernels.hip", "bwd_kernels.hip", "accept_kernels.hip"]
+HIP_SOURCES = ["attn_kernels.hip", "bwd_kernels.hip", "accept_kernels.hip", "calib_kernels.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]
 # Packed fp32 VALU ops are kept out of the device code on purpose.
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -492,3 +492,24 @@ extern "C" int tree_attn_accept(const ta_plan* plan, int32_t dtype, const void* 
 } catch (...) {
   return ta::fail_exception("accept");
 }
+
+extern "C" int tree_attn_calib_mfma(int32_t blocks, int32_t iters, float* sink, int64_t* flops, void* stream) try {
+  if (blocks <= 0 || blocks > (1 << 20) || iters <= 0 || iters > (1 << 24))
+    return fail(TA_ERR_INVALID_ARG, "calib_mfma: blocks must be in [1, 2^20] and iters in [1, 2^24]");
+  if (!sink || !aligned(sink, 4) || !flops) return fail(TA_ERR_INVALID_ARG, "calib_mfma: NULL or misaligned argument");
+  *flops = calib_mfma_flops(blocks, iters);
+  return hip_status(launch_calib_mfma(blocks, iters, sink, static_cast<hipStream_t>(stream)), "calib_mfma launch");
+} catch (...) {
+  return ta::fail_exception("calib_mfma");
+}
+
+extern "C" int tree_attn_calib_read(const void* src, int64_t bytes, int32_t blocks, uint32_t* sink,
+                                    void* stream) try {
+  if (!src || !aligned(src, 16) || bytes <= 0 || bytes % 16)
+    return fail(TA_ERR_INVALID_ARG, "calib_read: src must be 16-byte aligned and bytes a positive multiple of 16");
+  if (blocks <= 0 || blocks > (1 << 20) || !sink || !aligned(sink, 4))
+    return fail(TA_ERR_INVALID_ARG, "calib_read: blocks must be in [1, 2^20] with a 4-byte aligned sink");
+  return hip_status(launch_calib_read(src, bytes, blocks, sink, static_cast<hipStream_t>(stream)), "calib_read launch");
+} catch (...) {
+  return ta::fail_exception("calib_read");
+}

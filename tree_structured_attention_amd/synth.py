@@ -332,6 +332,30 @@ def config5(seed: int = 4, with_tensors: bool = True, n_pages: int = 64,
     return w
 
 
+def config5_unshared(seed: int = 4, nodes: int = 32) -> Workload:
+    """The verify workload's 512 draft trees, each over a prefix of its own
+    (P ~ U{4096..16384} per tree, no sharing between trees): 512 pages of one
+    branch each, about 5.2 M context tokens (21.7 GB of bf16 K/V).  Tensors
+    are drawn on the GPU (``verify_tensors_device``): the host would need
+    minutes for them."""
+    w = config5(seed, with_tensors=False, n_pages=512, branches_per_page=1, nodes=nodes)
+    w.name = f"verify_512_unshared_prefixes_x{nodes}nodes"
+    return w
+
+
+def verify_tensors_device(seed: int, desc: VerifyDesc, hq, hkv, d, dtype, device="cuda"):
+    """q, k_ctx, v_ctx, k_tree, v_tree ~ N(0, 1) drawn in that order by
+    torch's generator on `device` seeded with `seed` (for workloads too large
+    to draw on the host)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    c = int(desc.ctx_len.astype(np.int64).sum())
+    n = desc.total_nodes()
+    shapes = {"q": (n, hq, d), "k_ctx": (c, hkv, d), "v_ctx": (c, hkv, d), "k_tree": (n, hkv, d),
+              "v_tree": (n, hkv, d)}
+    return {k: torch.randn(sh, generator=g, device=device, dtype=torch.float32).to(dtype)
+            for k, sh in shapes.items()}
+
+
 # Vocabulary size of the Qwen-family decoders the pages build on; the pages
 # do not print it, so this is a stand-in for the logits width.
 VOCAB = 151936
