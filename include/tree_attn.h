@@ -368,6 +368,29 @@ int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv
                      void* o, float* lse, void* scratch, size_t scratch_bytes,
                      void* stream);
 
+/* Size of the device scratch tree_attn_decode_noalloc uses: 64 MiB, enough
+ * for 16 pages x 25 live rows x 8 new tokens at 16 query heads, d = 128. */
+#define TA_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as tree_attn_decode, with the same arguments except the scratch,
+ * whose fp32 partials live instead in a file-scope device array of
+ * TA_STATIC_SCRATCH_BYTES held on every GPU the library runs on until the
+ * process ends.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks the
+ * array's address up once (hipGetSymbolAddress, with that device current).
+ * Nothing in the array needs to start at zero: every partial the merge
+ * reads is written earlier in the same call.  All calls on one GPU share the
+ * array, which keeps the last call's contents, so calls that overlap on one
+ * GPU (other streams, other host threads) race: serialise them.  Errors: as
+ * tree_attn_decode, and CAPACITY when tree_attn_scratch_bytes for this plan
+ * and hq exceeds TA_STATIC_SCRATCH_BYTES (nothing is enqueued then). */
+int tree_attn_decode_noalloc(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
+                             int32_t head_dim, float scale, const void* q, const void* k_main,
+                             const void* v_main, const void* k_suffix, const void* v_suffix,
+                             void* o, float* lse, void* stream);
+
 /* Draft-tree verify over a verify plan.  q, o: [nodes, Hq, d];
  * k_ctx/v_ctx: [sum ctx_len, Hkv, d]; k_tree/v_tree: [nodes, Hkv, d];
  * scratch as for tree_attn_prefill. */

@@ -189,3 +189,22 @@ def test_host_allocation_failure_returns_capacity_status():
                        timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "out of host memory" in r.stdout and r.stdout.strip().endswith("ok"), r.stdout
+
+
+def test_decode_noalloc_host_checks():
+    """tree_attn_decode_noalloc checks on the host, before any device work: a
+    plan whose partials exceed TA_STATIC_SCRATCH_BYTES gets CAPACITY, a
+    plan that fits but is not uploaded gets STATE (fake, never dereferenced
+    16-byte aligned pointers stand in for the tensors)."""
+    import ctypes
+    L = ta.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    big = ta.plan_for(synth.decode_multi(with_tensors=False, window=40).desc)
+    assert ta.scratch_bytes(big, 16, 128) > ta.TA_STATIC_SCRATCH_BYTES
+    rc = L.tree_attn_decode_noalloc(big.handle, ta.TA_DTYPE_BF16, 16, 8, 128, 0.088, fake, fake, fake, fake, fake,
+                                    fake, None, None)
+    assert rc == ta.TA_ERR_CAPACITY and "static scratch" in ta.last_error()
+    small = ta.plan_for(synth.config4(with_tensors=False, n_pages=2).desc)
+    rc = L.tree_attn_decode_noalloc(small.handle, ta.TA_DTYPE_BF16, 16, 8, 128, 0.088, fake, fake, fake, fake,
+                                    fake, fake, None, None)
+    assert rc == ta.TA_ERR_STATE

@@ -137,6 +137,8 @@ def lib() -> ctypes.CDLL:
             "tree_attn_accept_scratch_bytes": ([_P, i64, ctypes.POINTER(sz)], ctypes.c_int),
             "tree_attn_accept": ([_P, i32, _P, i64, i64, _P, ctypes.c_double, i32, _P, _P, _P, _P, sz, _P],
                                  ctypes.c_int),
+            "tree_attn_decode_noalloc": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P, _P, _P],
+                                         ctypes.c_int),
             "tree_attn_calib_mfma": ([i32, i32, _P, _I64P, _P], ctypes.c_int),
             "tree_attn_calib_read": ([_P, i64, i32, _P, _P], ctypes.c_int),
             "tree_attn_last_error": ([], ctypes.c_char_p),
@@ -494,6 +496,24 @@ def decode(plan: Plan, q, k_main, v_main, k_suffix, v_suffix, scale=None, want_l
                                   _dev_ptr(k_main), _dev_ptr(v_main), _dev_ptr(k_suffix), _dev_ptr(v_suffix),
                                   _dev_ptr(o), _dev_ptr(l), sp, sn, _stream_handle(stream)))
     return o, l
+
+
+TA_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_noalloc(plan: Plan, q, k_main, v_main, k_suffix, v_suffix, out, lse=None, scale=None, stream=None):
+    """tree_attn_decode_noalloc: decode whose partials live in the library's
+    file-scope device scratch (the C call allocates nothing).  The caller
+    passes the outputs: out like q, lse fp32 [Hq, rows] or None."""
+    if out is None:
+        raise _bad("decode_noalloc writes into caller-provided outputs: pass out")
+    hq, hkv, d = _check_args(q, [(("k_main", k_main), ("v_main", v_main)),
+                                 (("k_suffix", k_suffix), ("v_suffix", v_suffix))], out=out, lse=lse)
+    _rows(plan, q, (k_main, v_main), (k_suffix, v_suffix))
+    _check(lib().tree_attn_decode_noalloc(plan.handle, _dtype_code(q), hq, hkv, d, _scale(scale, d), _dev_ptr(q),
+                                          _dev_ptr(k_main), _dev_ptr(v_main), _dev_ptr(k_suffix),
+                                          _dev_ptr(v_suffix), _dev_ptr(out), _dev_ptr(lse), _stream_handle(stream)))
+    return out, lse
 
 
 def verify(plan: Plan, q, k_ctx, v_ctx, k_tree, v_tree, scale=None, want_lse=True, out=None, lse=None,

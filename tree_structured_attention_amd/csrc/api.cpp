@@ -295,11 +295,12 @@ extern "C" int tree_attn_verify(const ta_plan* plan, int32_t dtype, int32_t hq, 
   return ta::fail_exception("verify");
 }
 
-extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim,
-                                float scale, const void* q, const void* k_main, const void* v_main,
-                                const void* k_suffix, const void* v_suffix, void* o, float* lse, void* scratch,
-                                size_t scratch_bytes, void* stream) try {
-  int rc = check_plan(plan, TA_PLAN_DECODE, "decode");
+namespace {
+
+int check_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                 const void* q, const void* k_main, const void* v_main, const void* k_suffix, const void* v_suffix,
+                 const void* o, const float* lse, const char* who) {
+  int rc = check_plan(plan, TA_PLAN_DECODE, who);
   if (rc) return rc;
   if ((rc = check_heads(dtype, hq, hkv, head_dim, scale))) return rc;
   const int64_t rows = plan->n_rows;
@@ -308,8 +309,12 @@ extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, 
       (rc = check_tensor(v_suffix, plan->n_keys_b, "v_suffix")) || (rc = check_tensor(o, rows, "o")))
     return rc;
   if (lse && !aligned(lse, 4)) return fail(TA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  if ((rc = check_scratch(plan, hq, head_dim, scratch, scratch_bytes, "decode"))) return rc;
-  if ((rc = check_uploaded(plan, "decode"))) return rc;
+  return TA_OK;
+}
+
+int launch_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                  const void* q, const void* k_main, const void* v_main, const void* k_suffix, const void* v_suffix,
+                  void* o, float* lse, void* scratch, void* stream) {
   AttnParams p = base_params(plan, hq, hkv, scale);
   p.q = q;
   p.ka = k_main;
@@ -320,11 +325,47 @@ extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, 
   p.lse = lse;
   set_partials(p, plan, hq, head_dim, scratch);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = hip_status(launch_attention(kDecode, dtype, p, int(plan->work.size()), head_dim, st), "decode launch");
+  int rc = hip_status(launch_attention(kDecode, dtype, p, int(plan->work.size()), head_dim, st), "decode launch");
   if (rc) return rc;
   return hip_status(launch_merge_for(plan, dtype, p, head_dim, st), "decode merge launch");
+}
+
+}  // namespace
+
+extern "C" int tree_attn_decode(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv, int32_t head_dim,
+                                float scale, const void* q, const void* k_main, const void* v_main,
+                                const void* k_suffix, const void* v_suffix, void* o, float* lse, void* scratch,
+                                size_t scratch_bytes, void* stream) try {
+  int rc = check_decode(plan, dtype, hq, hkv, head_dim, scale, q, k_main, v_main, k_suffix, v_suffix, o, lse,
+                        "decode");
+  if (rc) return rc;
+  if ((rc = check_scratch(plan, hq, head_dim, scratch, scratch_bytes, "decode"))) return rc;
+  if ((rc = check_uploaded(plan, "decode"))) return rc;
+  return launch_decode(plan, dtype, hq, hkv, head_dim, scale, q, k_main, v_main, k_suffix, v_suffix, o, lse,
+                       scratch, stream);
 } catch (...) {
   return ta::fail_exception("decode");
+}
+
+extern "C" int tree_attn_decode_noalloc(const ta_plan* plan, int32_t dtype, int32_t hq, int32_t hkv,
+                                        int32_t head_dim, float scale, const void* q, const void* k_main,
+                                        const void* v_main, const void* k_suffix, const void* v_suffix, void* o,
+                                        float* lse, void* stream) try {
+  int rc = check_decode(plan, dtype, hq, hkv, head_dim, scale, q, k_main, v_main, k_suffix, v_suffix, o, lse,
+                        "decode_noalloc");
+  if (rc) return rc;
+  const int64_t need = scratch_need(plan, hq, head_dim);
+  if (need > int64_t(TA_STATIC_SCRATCH_BYTES))
+    return fail(TA_ERR_CAPACITY, "decode_noalloc: the plan needs " + std::to_string(need) +
+                                     " bytes of scratch; the static scratch holds " +
+                                     std::to_string(int64_t(TA_STATIC_SCRATCH_BYTES)) + " (use tree_attn_decode)");
+  if ((rc = check_uploaded(plan, "decode_noalloc"))) return rc;
+  void* scratch = nullptr;
+  if (need > 0 && (rc = hip_status(static_scratch(&scratch), "decode_noalloc: static scratch"))) return rc;
+  return launch_decode(plan, dtype, hq, hkv, head_dim, scale, q, k_main, v_main, k_suffix, v_suffix, o, lse,
+                       scratch, stream);
+} catch (...) {
+  return ta::fail_exception("decode_noalloc");
 }
 
 namespace {

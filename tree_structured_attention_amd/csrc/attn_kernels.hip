@@ -32,6 +32,8 @@
 // unless it is a non-finite V of a key another row of the same tile needs.
 // fp32 inputs use v_mfma_f32_32x32x2f32 with the same tiling (no
 // down-conversion).
+#include <mutex>
+
 #include "ta_device.h"
 
 namespace ta {
@@ -517,6 +519,39 @@ TA_INSTANTIATE(float, 64, 2)
 TA_INSTANTIATE(float, 128, 1)
 TA_INSTANTIATE(float, 128, 2)
 #undef TA_INSTANTIATE
+
+// ---------------------------------------------------------------------------
+// file-scope scratch of the allocation-free decode entry point
+// ---------------------------------------------------------------------------
+
+// fp32 partials of tree_attn_decode_noalloc: one copy per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[TA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // ---------------------------------------------------------------------------
 // host launchers

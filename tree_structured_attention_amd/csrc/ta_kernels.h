@@ -93,6 +93,9 @@ hipError_t launch_attention(int mode, int dtype, const AttnParams& p, int n_work
 hipError_t launch_merge(int dtype, const MergeParams& p, int head_dim, hipStream_t st);
 hipError_t launch_backward(const BwdParams& p, int n_work, int n_kwork, int n_kmerge, int head_dim, hipStream_t st);
 hipError_t launch_accept(int dtype, const AcceptParams& p, int64_t n_rows, hipStream_t st);
+// Device address of the file-scope scratch (TA_STATIC_SCRATCH_BYTES) on the
+// current device, looked up on the first call per device.
+hipError_t static_scratch(void** ptr);
 hipError_t launch_calib_mfma(int32_t blocks, int32_t iters, float* sink, hipStream_t st);
 hipError_t launch_calib_read(const void* src, int64_t bytes, int32_t blocks, uint32_t* sink, hipStream_t st);
 int64_t calib_mfma_flops(int32_t blocks, int32_t iters);
