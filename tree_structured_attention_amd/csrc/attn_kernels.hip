@@ -88,16 +88,13 @@ struct RowState {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[bk][i] = 0.f;
     if constexpr (kBf) {
-      // The k-steps of a lane's K row differ only in XOR-swizzled chunk
-      // bits: koff[st] = koff[0] ^ 16 st.  The empty asm keeps the XORs here
-      // instead of eight registers hoisted out of the tile loop.
-      int kx = koff[0];
-      asm volatile("" : "+v"(kx));
+      // the lane's K-row offsets of all k-steps stay in registers (computed
+      // once per work item): no address arithmetic per tile
 #pragma unroll
       for (int st = 0; st < kQSteps; ++st)
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + (kx ^ (16 * st)) + 32 * bk * G::kRowBytes);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + koff[st] + 32 * bk * G::kRowBytes);
           s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[bk], 0, 0, 0);
         }
       sched_ld_mfma<0, 2 * kQSteps, 1, 4>();
@@ -158,8 +155,6 @@ struct RowState {
       l_run += ls;
 
       // ---- O^T += V^T P^T ----
-      int vx = voff[0];
-      if constexpr (D == 128) asm volatile("" : "+v"(vx));  // as for kx above
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
@@ -168,8 +163,8 @@ struct RowState {
           const unsigned char* vb = vl + (32 * bk + 16 * c2) * G::kRowBytes;
 #pragma unroll
           for (int md = 0; md < kDB; ++md) {
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + vread_off(vx, 0, md)));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + vread_off(vx, 1, md)));
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + voff[md]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + voff[kDB + md]));
             const s16x4 both[2] = {lo, hi};
             const bf16x8 a = __builtin_bit_cast(bf16x8, both);
             acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[md], 0, 0, 0);
@@ -247,29 +242,26 @@ struct RowState {
 
   // bf16: P = exp2(c s - c m) as bf16 pairs, the P^T operands of the PV
   // MFMAs (pw[bk][c2]: keys 16 c2.. of 32-key block bk); returns the lane's
-  // part of the row sum.
+  // part of the row sum, taken over the rounded pairs with one
+  // v_dot2_f32_bf16 each (so the normaliser sums exactly the weights the PV
+  // product multiplies), in two chains.
   __device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], u32x4 (&pw)[2][2]) const {
     const float mb = (m_used == -INFINITY) ? 0.f : m_used * c;
-    float ls = 0.f;
+    const bf16x2v ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    float ls[2] = {0.f, 0.f};
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float e0 = fast_exp2(fmaf(s[bk][2 * j], c, -mb));
         const float e1 = fast_exp2(fmaf(s[bk][2 * j + 1], c, -mb));
-        ls += e0 + e1;
-        pw[bk][j >> 2][j & 3] = pack_bf16x2(e0, e1);
+        const uint32_t pk = pack_bf16x2(e0, e1);
+        pw[bk][j >> 2][j & 3] = pk;
+        ls[j & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pk), ones, ls[j & 1], false);
       }
-    return ls;
+    return ls[0] + ls[1];
   }
 
-  // Byte offset of the transposing V read (r, md) of this lane.  At
-  // head_dim 128 the reads differ only in swizzled chunk bits and a 4-row
-  // step: voff(r, md) = (voff(0, 0) ^ (64 md + 16 r)) + 4 r rows.
-  __device__ __forceinline__ int vread_off(int vx, int r, int md) const {
-    if constexpr (D == 128) return (vx ^ (64 * md + 16 * r)) + r * 4 * G::kRowBytes;
-    else return voff[r * kDB + md];
-  }
 };
 
 // ---------------------------------------------------------------------------

@@ -92,13 +92,23 @@ struct TileGeom {
   }
 };
 
-// The same tile for 16x16x32 operand reads (the key-major backward): there
-// a transposing read gives lane group g rows 4 g .. 4 g + 3 of a 16-row block
-// at 16 consecutive d (one chunk pair), and groups g, g + 1 are served
-// together, so rows r and r + 4 must not share banks for a chunk pair:
-//   swz(row) = 2 ((row / P) mod (chunks / 2)) + (row / 8) mod 2,
-// with P rows per 256-byte bank period.  The 16 rows of a 16x16x32 operand
-// read still land in distinct chunk positions of their bank period.
+// The same tile for 16x16x32 operand reads (the key-major backward).  Two
+// read patterns meet in it:
+//  * a transposing read gives lane group g (16 lanes) rows 4 g .. 4 g + 3 of
+//    a 16-row block at 16 consecutive d (one chunk pair), and 32 lanes are
+//    served per cycle, so the 8 rows of groups g, g + 1 need distinct chunk
+//    pairs: swz(row) / 2 must differ over every 8 aligned rows;
+//  * a 16-byte operand read gives lane l row l % 16 at chunk l / 16 (+ 4 per
+//    k-step).  On gfx950 such a read serves 16 lanes per cycle, grouped by
+//    lane bit 5 and the parity of lane bits 2..4 (measured: only lane pairs
+//    within such a group raise the bank-conflict counter), so one group
+//    holds each row once but chunk l / 16 flips with the parity of row bits
+//    2, 3; positions stay distinct when swz's low bit carries row bit 2.
+// At 16 chunks per row both hold for swz(row) = 2 (row mod 8) + (row / 4)
+// mod 2 (no bank conflicts left in the dK/dV kernel, measured; the earlier
+// low bit (row / 8) mod 2 left every 16-byte read 2-way conflicted).
+// Narrower rows (P rows per 256-byte bank period) keep
+//   swz(row) = 2 ((row / P) mod (chunks / 2)) + (row / 8) mod 2.
 template <typename T, int D>
 struct TileGeomB {
   static constexpr int kRowBytes = D * Elt<T>::kBytes;
@@ -107,7 +117,8 @@ struct TileGeomB {
   static constexpr int kStageBytes = 2 * kTileBytes;
   static constexpr int kPeriod = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
   __device__ static __forceinline__ int swz(int row) {
-    return ((((row / kPeriod) & (kChunks / 2 - 1)) << 1) | ((row >> 3) & 1)) & (kChunks - 1);
+    if constexpr (kChunks == 16) return ((row & 7) << 1) | ((row >> 2) & 1);
+    else return ((((row / kPeriod) & (kChunks / 2 - 1)) << 1) | ((row >> 3) & 1)) & (kChunks - 1);
   }
   __device__ static __forceinline__ int at(int row, int byte) {
     return row * kRowBytes + ((((byte >> 4) ^ swz(row)) << 4) | (byte & 15));
