@@ -259,12 +259,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
 
   TileLoader<T, D, NW, 0, G> loader;
   loader.init(lane, wave, q_stride);
-  // step s = (query head j of the group, row tile r of the piece): the Q and
-  // dO tiles and the tile's row values go to the stage by DMA; wave w copies
-  // row-value array w of RowMeta (lse2, Dd, row_a, row_b), and rows past the
-  // segment end read as 0
-  auto issue = [&](int s, unsigned char* stage) {
-    const int j = s / n_pc, r = wi.tile_lo + s % n_pc;
+  // step = (query head j of the group, row tile r of the piece), heads
+  // outer: the Q and dO tiles and the tile's row values go to the stage by
+  // DMA; wave w copies row-value array w of RowMeta (lse2, Dd, row_a, row_b),
+  // and rows past the segment end read as 0
+  auto issue = [&](int j, int r, unsigned char* stage) {
     const int head = kvh * p.group + j;
     const unsigned char* qb = reinterpret_cast<const unsigned char*>(p.q) + int64_t(head) * D * 2;
     const unsigned char* gb = reinterpret_cast<const unsigned char*>(p.dO) + int64_t(head) * D * 2;
@@ -316,11 +315,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
       dv[db][i] = 0.f;
     }
 
-  auto consume = [&](const unsigned char* stage, int s) {
+  auto consume = [&](const unsigned char* stage, int r) {
     const unsigned char* qt = stage;
     const unsigned char* gt = stage + G::kTileBytes;
     const RowMeta* m = reinterpret_cast<const RowMeta*>(stage + G::kStageBytes);
-    const int r = wi.tile_lo + s % n_pc;
     const int r0 = rt0(r), rhi = rt_hi(r);
     // row tiles past the segment's first fully visible row need no test
     // (rows past the segment end hold zero Q, dO, lse2 and Dd: they add 0)
@@ -389,12 +387,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  if (n_steps > 0) issue(0, lds0);
+  // (head, row tile) of the next step to copy and of the step consumed,
+  // advanced by counting rather than by a division per step
+  int j_in = 0, r_in = wi.tile_lo, r_cur = wi.tile_lo;
+  auto advance_in = [&]() {
+    if (++r_in == wi.tile_hi) {
+      r_in = wi.tile_lo;
+      ++j_in;
+    }
+  };
+  if (n_steps > 0) {
+    issue(j_in, r_in, lds0);
+    advance_in();
+  }
   auto step = [&](int s, unsigned char* cur, unsigned char* nxt) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's copies into cur are done
     __syncthreads();                     // ... and every wave's; reads of nxt are retired
-    if (s + 1 < n_steps) issue(s + 1, nxt);
-    consume(cur, s);
+    if (s + 1 < n_steps) {
+      issue(j_in, r_in, nxt);
+      advance_in();
+    }
+    consume(cur, r_cur);
+    if (++r_cur == wi.tile_hi) r_cur = wi.tile_lo;
   };
 #pragma unroll 1
   for (int s = 0; s < n_steps; s += 2) {

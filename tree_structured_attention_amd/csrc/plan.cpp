@@ -41,6 +41,26 @@ void order_work(std::vector<WorkItem>& w) {
                    [](const WorkItem& x, const WorkItem& y) { return item_cost(x) > item_cost(y); });
 }
 
+// Prefill: pages in order, each page's items longest first.  Every item of
+// a KV head runs on that head's XCD (workgroup x = item * Hkv + head, and
+// workgroups go round-robin over the 8 XCDs), so with this order an XCD's
+// slots work on one or two pages at a time and the K/V those row tiles
+// re-read stays in its 4 MB L2.  Longest first over all pages mixed the
+// row tiles of every page on each XCD: 4.4 GB of HBM traffic per launch
+// for the 8-page batch (0.95 GB algorithmic) against 1.28 GB in page order.
+void order_work_paged(std::vector<WorkItem>& w, const std::vector<int64_t>& pages5) {
+  std::vector<int64_t> base;
+  for (size_t i = 0; i < pages5.size(); i += 5) base.push_back(pages5[i]);
+  auto page_of = [&](int32_t row) {
+    return int(std::upper_bound(base.begin(), base.end(), int64_t(row)) - base.begin()) - 1;
+  };
+  std::stable_sort(w.begin(), w.end(), [&](const WorkItem& x, const WorkItem& y) {
+    const int px = page_of(x.row0), py = page_of(y.row0);
+    if (px != py) return px < py;
+    return item_cost(x) > item_cost(y);
+  });
+}
+
 WorkItem make_item(int64_t row0, int64_t nrows, int64_t a_lo, int64_t a_full, int64_t a_hi,
                    int64_t b_lo, int64_t b_hi, int64_t out, int32_t flags) {
   WorkItem w{};
@@ -315,7 +335,7 @@ extern "C" int tree_attn_plan_prefill(const int32_t* prefix_len, const int32_t* 
     pl->row_a[i] = int32_t(pl->main_end[i]);
     pl->row_b[i] = int32_t(pl->branch_start[i]);
   }
-  order_work(pl->work);
+  order_work_paged(pl->work, pl->pages5);
   pack_blob(pl);
   *out = owner.release();
   return TA_OK;
@@ -785,7 +805,8 @@ extern "C" int tree_attn_plan_balance(ta_plan* plan, int32_t n_kv_heads, int32_t
     slot += int64_t(n_pieces[item]) * w.nrows;
     if (slot >= kMax32) return fail(TA_ERR_CAPACITY, "plan_balance: partial slots >= 2^31");
   }
-  order_work(out);
+  if (plan->kind == TA_PLAN_PREFILL) order_work_paged(out, plan->pages5);
+  else order_work(out);
   plan->work.swap(out);
   plan->merge.swap(merge);
   const int64_t old_partials = plan->n_partials;
