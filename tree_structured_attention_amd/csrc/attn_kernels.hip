@@ -111,28 +111,30 @@ struct RowState {
 
     // ---- visibility: selection to -inf, only on tiles that need it ----
     if (masked) {
-      const int kbase = t0 + 8 * h;
+      // the row's visible keys of this tile, [lo, hi) and (verify, tree
+      // segment) its ancestor bits, as one mask over the lane's key offsets;
+      // a row past the item's end keeps every key below t_hi
+      const int base = t0 + 8 * h;
+      int lo = base, hi = t_hi;
+      uint64_t tree = ~0ull;
+      if (seg_a) {
+        if constexpr (MODE != kVerify) hi = row_ok ? min(hi, ra) : hi;
+      } else {
+        if constexpr (MODE == kPrefill) {
+          lo = row_ok ? max(lo, rb) : lo;
+          hi = row_ok ? min(hi, row + 1) : hi;
+        } else if constexpr (MODE == kDecode) {
+          hi = row_ok ? min(hi, rb) : hi;
+        } else {
+          tree = row_ok ? shift_bits(rmask, base - rb) : ~0ull;
+        }
+      }
+      const uint64_t vis = bit_range(lo - base, hi - base) & tree;
+      const uint32_t w[2] = {uint32_t(vis), uint32_t(vis >> 32)};
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase + 32 * bk + 16 * (i >> 3) + (i & 7);
-          bool vis = key < t_hi;
-          if (seg_a) {
-            if constexpr (MODE != kVerify) vis = vis & (!row_ok | (key < ra));
-          } else {
-            if constexpr (MODE == kPrefill) {
-              vis = vis & (!row_ok | ((key >= rb) & (key <= row)));
-            } else if constexpr (MODE == kDecode) {
-              vis = vis & (!row_ok | (key < rb));
-            } else if constexpr (MODE == kVerify) {
-              const unsigned rel = unsigned(key - rb);
-              const uint32_t word = rel < 32u ? uint32_t(rmask) : uint32_t(rmask >> 32);
-              vis = vis & (!row_ok | ((rel < 64u) & (((word >> (rel & 31u)) & 1u) != 0u)));
-            }
-          }
-          s[bk][i] = vis ? s[bk][i] : -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i) s[bk][i] = pick_bit(s[bk][i], w[bk], 16 * (i >> 3) + (i & 7), -INFINITY);
     }
 
     if constexpr (kBf) {

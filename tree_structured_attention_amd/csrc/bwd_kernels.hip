@@ -141,6 +141,17 @@ __global__ __launch_bounds__(128 * GH, 2) void bwd_dq_kernel(BwdParams p) {
     const bool seg_a = it < n_a;
     const int t0 = tile0(it), t_hi = tile_hi(it);
     const bool masked = seg_a ? it >= fa : true;
+    // masked tiles: the row's visible keys [lo, hi) of this tile as a mask
+    // over the lane's key offsets (as in the forward)
+    uint32_t w[2] = {~0u, ~0u};
+    if (masked) {
+      const int base = t0 + 8 * h;
+      const int lo = seg_a ? base : max(base, rb);
+      const int hi = seg_a ? min(t_hi, ra) : min(t_hi, row + 1);
+      const uint64_t vis = bit_range(lo - base, hi - base);
+      w[0] = uint32_t(vis);
+      w[1] = uint32_t(vis >> 32);
+    }
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk) {
       f32x16 s = {}, dp = {};
@@ -151,7 +162,17 @@ __global__ __launch_bounds__(128 * GH, 2) void bwd_dq_kernel(BwdParams p) {
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vl + off), df[st], dp, 0, 0, 0);
       }
       sched_ld_mfma<0, 2 * kQSteps, 1, 4>();
-      // dS^T = P^T (dP^T - Dd), P^T = 2^(s c - lse2); invisible pairs get 0
+      // invisible pairs: s -> -inf (P = 0) and dP -> Dd, so dS is exactly 0
+      // whatever the key's values
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = 16 * (i >> 3) + (i & 7);
+          s[i] = pick_bit(s[i], w[bk], c, -INFINITY);
+          dp[i] = pick_bit(dp[i], w[bk], c, dd);
+        }
+      }
+      // dS^T = P^T (dP^T - Dd), P^T = 2^(s c - lse2)
       u32x4 pk[2];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -159,15 +180,7 @@ __global__ __launch_bounds__(128 * GH, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int i = 2 * j + e;
-          const int key = t0 + 32 * bk + reg_key(i, h);
-          bool vis = true;
-          if (masked) {
-            vis = key < t_hi;
-            if (seg_a) vis = vis & (key < ra);
-            else vis = vis & (key >= rb) & (key <= row);
-          }
-          const float pr = vis ? fast_exp2(fmaf(s[i], p.c, -l2)) : 0.f;
-          ds[e] = pr * (dp[i] - dd);
+          ds[e] = fast_exp2(fmaf(s[i], p.c, -l2)) * (dp[i] - dd);
         }
         pk[j >> 2][j & 3] = pack_bf16x2(ds[0], ds[1]);
       }
@@ -343,21 +356,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
         const float4 l2 = *reinterpret_cast<const float4*>(&m->l2[lr]);
         const float4 dd = *reinterpret_cast<const float4*>(&m->dd[lr]);
         const float l2v[4] = {l2.x, l2.y, l2.z, l2.w}, ddv[4] = {dd.x, dd.y, dd.z, dd.w};
-        bool vis[4] = {true, true, true, true};
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = fmaf(sc[i], p.c, -l2v[i]);
         if (masked) {
+          // the row sees this lane's key when key is in [lo, hi): [row_b, row]
+          // for branch keys, below row_a for main keys; an invisible pair
+          // gets P = 0 and dP = Dd, so it adds exactly 0
           const int4 ra4 = *reinterpret_cast<const int4*>(&m->ra[lr]);
           const int4 rb4 = *reinterpret_cast<const int4*>(&m->rb[lr]);
           const int ra[4] = {ra4.x, ra4.y, ra4.z, ra4.w}, rbv[4] = {rb4.x, rb4.y, rb4.z, rb4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int row = r0 + lr + i;
-            vis[i] = (row < rhi) & (branch_keys ? ((key >= rbv[i]) & (key <= row)) : (key < ra[i]));
+            const int lo = branch_keys ? rbv[i] : INT32_MIN;
+            const int hi = branch_keys ? row + 1 : ra[i];
+            const bool vis = (row < rhi) & (key >= lo) & (key < hi);
+            x[i] = vis ? x[i] : -INFINITY;
+            dp[i] = vis ? dp[i] : ddv[i];
           }
         }
         float pr[4], ds[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pr[i] = vis[i] ? fast_exp2(fmaf(sc[i], p.c, -l2v[i])) : 0.f;
+          pr[i] = fast_exp2(x[i]);
           ds[i] = pr[i] * (dp[i] - ddv[i]);
         }
         pp[2 * b1] = pack_bf16x2(pr[0], pr[1]);

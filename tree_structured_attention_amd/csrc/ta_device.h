@@ -46,6 +46,28 @@ __device__ __forceinline__ int key_perm(int m) {
 // physical key 16 * (i / 8) + 8 * h + (i % 8).
 __device__ __forceinline__ int reg_key(int i, int h) { return 16 * (i >> 3) + 8 * h + (i & 7); }
 
+// Visibility of a lane's scores in a 64-key tile as a 64-bit mask: bit o
+// stands for the key at offset o from the lane's first key (the tile's first
+// key + 8 h), so accumulator register i of 32-key block bk is bit
+// 32 bk + 16 (i / 8) + (i % 8).
+// Bits [a, b) with a and b clamped to [0, 64].
+__device__ __forceinline__ uint64_t bit_range(int a, int b) {
+  auto below = [](int n) -> uint64_t { return n >= 64 ? ~0ull : n <= 0 ? 0ull : (1ull << n) - 1; };
+  return below(b) & ~below(a);
+}
+// Bits of `m` moved down by `sh` (up by -sh when negative), 0 when |sh| >= 64.
+__device__ __forceinline__ uint64_t shift_bits(uint64_t m, int sh) {
+  if (sh >= 0) return sh < 64 ? m >> sh : 0ull;
+  return sh > -64 ? m << -sh : 0ull;
+}
+// x where bit c of w is set, else `alt`: the sign-extended one-bit field is
+// all ones or all zeros and picks between the two bit patterns, so a masked
+// tile needs two vector instructions per score and no lane-mask compares.
+__device__ __forceinline__ float pick_bit(float x, uint32_t w, int c, float alt) {
+  const uint32_t m = uint32_t(__builtin_amdgcn_sbfe(int(w), uint32_t(c), 1u));
+  return __uint_as_float((__float_as_uint(x) & m) | (__float_as_uint(alt) & ~m));
+}
+
 typedef __attribute__((ext_vector_type(2))) float f32x2v;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
 
