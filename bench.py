@@ -259,7 +259,7 @@ def backward_case():
     bytes_ = rows * (4 * w.hq + 4 * w.hkv) * w.head_dim * 2 + rows * w.hq * 4
     return dict(name="backward", w=w, plan=plan, run=run, unit_count=rows, unit="packed tokens",
                 flops=flops, bytes=bytes_, bound="mfma", plan_us=0.0, in_step=False,
-                kernel="bwd_prep_kernel<128> + bwd_dq_kernel<128,2> + bwd_dkdv_kernel<128>")
+                kernel="bwd_prep_kernel<128> + bwd_fused_kernel<128> (row tiles, then key tiles) + bwd_kmerge_kernel<128>")
 
 
 def accept_case():

@@ -17,6 +17,10 @@
 //                     adding dO^T P into dV^T and Q^T dS into dK^T; a long
 //                     walk comes as pieces that write fp32 partials
 //   bwd_kmerge_kernel the partials of each split key tile summed in order
+// With query heads in pairs (hq / hkv even) the two passes go out as one
+// launch, bwd_fused_kernel: the row tiles first, then the key-major items, so
+// one pass's long items and the other's short ones share the GPU instead of
+// each launch ending on a tail of its own.
 // Both main kernels pair an operand read from an LDS tile against one held
 // in registers, and a transposing LDS read (ds_read_b64_tr_b16) against a
 // product taken straight from accumulators: 32x32x16 bf16 MFMAs in the
@@ -59,23 +63,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 // dQ: query-major
 // ---------------------------------------------------------------------------
 
-// GH query heads of one KV head per workgroup, 32 / GH tokens per wave, a
-// 64-token row tile per work item (the forward's tiling and segments).
+// GH query heads of one KV head per workgroup (heads GH hy .. of the
+// group), 32 / GH tokens per wave, a 64-token row tile per work item (the
+// forward's tiling and segments); two LDS stages of TileGeom<bf16, D>.
 template <int D, int GH>
-__global__ __launch_bounds__(128 * GH, 2) void bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_dq_body(const BwdParams& p, unsigned char* lds0, unsigned char* lds1, int kvh,
+                                            int item, int hy) {
   using T = __bf16;
   using G = TileGeom<T, D>;
   constexpr int NW = 2 * GH;
   constexpr int TPW = 32 / GH;
   constexpr int kQSteps = D / 16;
   constexpr int kDB = D / 32;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds0[G::kStageBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds1[G::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int kvh = int(blockIdx.x % unsigned(p.hkv));
-  const WorkItem wi = p.work[blockIdx.x / unsigned(p.hkv)];
+  const WorkItem wi = p.work[item];
   const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
   const int n_tiles = n_a + (wi.b_hi - wi.b_lo + kKeyTile - 1) / kKeyTile;
   const int fa = min(n_a, max(0, wi.a_full - wi.a_lo) / kKeyTile);
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(128 * GH, 2) void bwd_dq_kernel(BwdParams p) {
 
   const int h = lane >> 5, n = lane & 31;
   const int tok = wave * TPW + n / GH;
-  const int head = kvh * p.group + int(blockIdx.y) * GH + (n % GH);
+  const int head = kvh * p.group + hy * GH + (n % GH);
   const bool row_ok = tok < wi.nrows;
   const int row = wi.row0 + tok;
   int ra = 0, rb = 0;
@@ -247,21 +250,24 @@ struct RowMeta {
 //     of transposing LDS reads (rows 4 (l / 16) .. +3 of each 16-row block at
 //     16 consecutive d), the B operand the lane's own P / dS values of those
 //     two blocks, packed in the same row order.
+// Two LDS stages of DkdvStage<D>::kBytes: a TileGeomB<bf16, D> Q / dO tile
+// pair and the tile's RowMeta.
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
+struct DkdvStage {
+  static constexpr int kBytes = TileGeomB<__bf16, D>::kStageBytes + int(sizeof(RowMeta));
+};
+template <int D>
+__device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, unsigned char* lds0, unsigned char* lds1, int kvh,
+                                              int item) {
   using T = __bf16;
   using G = TileGeomB<T, D>;
   constexpr int NW = 4;
   constexpr int kKS = D / 32;  // k-steps of 32 over head_dim
   constexpr int kDB = D / 16;  // 16-wide blocks of head_dim
-  constexpr int kStage = G::kStageBytes + int(sizeof(RowMeta));
-  __shared__ __attribute__((aligned(1024))) unsigned char lds0[kStage];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds1[kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int kvh = int(blockIdx.x % unsigned(p.hkv));
-  const WorkItem wi = p.kwork[blockIdx.x / unsigned(p.hkv)];
+  const WorkItem wi = p.kwork[item];
   const bool branch_keys = (wi.flags & kKeyBranch) != 0;
   const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
   const int n_pc = wi.tile_hi - wi.tile_lo;  // this piece's row tiles per query head
@@ -488,13 +494,48 @@ __global__ __launch_bounds__(256) void bwd_kmerge_kernel(BwdParams p) {
   }
 }
 
+// The query-major pass alone (one query head per KV head: two-wave groups).
+template <int D, int GH>
+__global__ __launch_bounds__(128 * GH, 2) void bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * TileGeom<__bf16, D>::kStageBytes];
+  bwd_dq_body<D, GH>(p, lds, lds + TileGeom<__bf16, D>::kStageBytes, int(blockIdx.x % unsigned(p.hkv)),
+                     int(blockIdx.x / unsigned(p.hkv)), int(blockIdx.y));
+}
+
+// The key-major pass alone.
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * DkdvStage<D>::kBytes];
+  bwd_dkdv_body<D>(p, lds, lds + DkdvStage<D>::kBytes, int(blockIdx.x % unsigned(p.hkv)),
+                   int(blockIdx.x / unsigned(p.hkv)));
+}
+
+// Both passes in one launch (query heads in pairs): workgroups [0, n_dq)
+// take the query-major row tiles (heads pair by pair), the rest the key-major
+// items.  The row tiles come first, longest first, so the key-major items
+// fill the slots their tail leaves and the launch ends on short pieces.
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_fused_kernel(BwdParams p, int n_dq) {
+  constexpr int kA = TileGeom<__bf16, D>::kStageBytes, kB = DkdvStage<D>::kBytes;
+  constexpr int kStage = kA > kB ? kA : kB;
+  static_assert(kStage % 1024 == 0, "stages start on 1 KB boundaries");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
+  const int b = int(blockIdx.x), kvh = b % p.hkv;
+  if (b < n_dq) {
+    const int t = b / p.hkv, ny = p.group / 2;
+    bwd_dq_body<D, 2>(p, lds, lds + kStage, kvh, t / ny, t % ny);
+  } else {
+    bwd_dkdv_body<D>(p, lds, lds + kStage, kvh, (b - n_dq) / p.hkv);
+  }
+}
+
 template __global__ void bwd_prep_kernel<32>(BwdParams);
 template __global__ void bwd_prep_kernel<64>(BwdParams);
 template __global__ void bwd_prep_kernel<128>(BwdParams);
 #define TA_INSTANTIATE_BWD(D)                              \
   template __global__ void bwd_dq_kernel<D, 1>(BwdParams); \
-  template __global__ void bwd_dq_kernel<D, 2>(BwdParams); \
-  template __global__ void bwd_dkdv_kernel<D>(BwdParams); \
+  template __global__ void bwd_dkdv_kernel<D>(BwdParams);   \
+  template __global__ void bwd_fused_kernel<D>(BwdParams, int); \
   template __global__ void bwd_kmerge_kernel<D>(BwdParams);
 TA_INSTANTIATE_BWD(32)
 TA_INSTANTIATE_BWD(64)
@@ -505,15 +546,16 @@ template <int D>
 static hipError_t launch_bwd_d(const BwdParams& p, int n_work, int n_kwork, int n_kmerge, hipStream_t st) {
   const int64_t pairs = p.n_rows * p.hq;
   if (pairs > 0) hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(unsigned((pairs + 3) / 4)), dim3(256), 0, st, p);
-  if (n_work > 0) {
-    if (p.group == 1)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, 1>), dim3(unsigned(n_work) * unsigned(p.hkv), 1u), dim3(128), 0, st, p);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), dim3(unsigned(n_work) * unsigned(p.hkv), unsigned(p.group / 2)),
-                         dim3(256), 0, st, p);
+  if (p.group == 1) {
+    if (n_work > 0)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 1>), dim3(unsigned(n_work) * unsigned(p.hkv)), dim3(128), 0, st, p);
+    if (n_kwork > 0)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(unsigned(n_kwork) * unsigned(p.hkv)), dim3(256), 0, st, p);
+  } else if (n_work + n_kwork > 0) {
+    const int64_t n_dq = int64_t(n_work) * p.hkv * (p.group / 2);
+    const int64_t n_blocks = n_dq + int64_t(n_kwork) * p.hkv;
+    hipLaunchKernelGGL((bwd_fused_kernel<D>), dim3(unsigned(n_blocks)), dim3(256), 0, st, p, int(n_dq));
   }
-  if (n_kwork > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(unsigned(n_kwork) * unsigned(p.hkv)), dim3(256), 0, st, p);
   if (n_kmerge > 0)
     hipLaunchKernelGGL((bwd_kmerge_kernel<D>), dim3(unsigned(n_kmerge) * unsigned(p.hkv)), dim3(256), 0, st, p);
   return hipGetLastError();
