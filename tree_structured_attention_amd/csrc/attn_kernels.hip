@@ -290,7 +290,9 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[G::kStageBytes];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar: per-wave LDS addresses (the copies' M0) stay in
+  // scalar registers
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kvh = int(blockIdx.x % unsigned(p.hkv));
   const WorkItem wi = p.work[blockIdx.x / unsigned(p.hkv)];
 

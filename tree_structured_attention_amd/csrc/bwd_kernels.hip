@@ -77,7 +77,9 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p, unsigned char* l
   constexpr int kDB = D / 32;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar: per-wave LDS addresses (the copies' M0) stay in
+  // scalar registers
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const WorkItem wi = p.work[item];
   const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
   const int n_tiles = n_a + (wi.b_hi - wi.b_lo + kKeyTile - 1) / kKeyTile;
@@ -266,7 +268,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p, unsigned char*
   constexpr int kDB = D / 16;  // 16-wide blocks of head_dim
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar: per-wave LDS addresses (the copies' M0) stay in
+  // scalar registers
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const WorkItem wi = p.kwork[item];
   const bool branch_keys = (wi.flags & kKeyBranch) != 0;
   const int n_a = (wi.a_hi - wi.a_lo + kKeyTile - 1) / kKeyTile;
