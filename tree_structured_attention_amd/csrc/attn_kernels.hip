@@ -51,6 +51,8 @@ struct RowState {
   QFrag qf[kQSteps];
   f32x16 acc[kDB];
   float m_used;  // exp2 base in raw-score units: a maximum of the scores so far (bf16: may lag the current one)
+  float mbc;     // bf16: the exp2 offset m_used * c (0 while the base is unset), kept beside m_used
+  bool unset;    // wave-uniform: some row of the wave has no base yet (bases never return to unset)
   float l_run;   // this lane's half of the row sum
   int koff[kBf ? kQSteps : 1];
   int voff[kBf ? 2 * kDB : 1];
@@ -144,7 +146,10 @@ struct RowState {
       // the base, or an overflow) moves its base to its maximum, and P is
       // taken again (rare).  The base lags the true maximum by less than
       // 2^16 in P, far inside fp32 and bf16 range. ----
-      if (__any(m_used == -INFINITY)) rebase(s, false);
+      if (unset) {
+        if (__any(m_used == -INFINITY)) rebase(s, false);
+        unset = __any(m_used == -INFINITY);
+      }
       u32x4 pw[2][2];
       float ls = exp_pack(s, pw);
       // the decision is the row's own (both lanes of a row see the same
@@ -240,6 +245,7 @@ struct RowState {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[md][i] *= alpha;
     m_used = m_new;
+    mbc = (m_used == -INFINITY) ? 0.f : m_used * c;
   }
 
   // bf16: P = exp2(c s - c m) as bf16 pairs, the P^T operands of the PV
@@ -248,7 +254,7 @@ struct RowState {
   // v_dot2_f32_bf16 each (so the normaliser sums exactly the weights the PV
   // product multiplies), in two chains.
   __device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], u32x4 (&pw)[2][2]) const {
-    const float mb = (m_used == -INFINITY) ? 0.f : m_used * c;
+    const float mb = mbc;
     const bf16x2v ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
     float ls[2] = {0.f, 0.f};
 #pragma unroll
@@ -361,6 +367,8 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   rs.c = p.c;
   rs.tau = 8.f / p.c;
   rs.m_used = -INFINITY;
+  rs.mbc = 0.f;
+  rs.unset = true;
   rs.l_run = 0.f;
   rs.init_offsets(lane);
 
