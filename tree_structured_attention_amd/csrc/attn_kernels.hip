@@ -56,7 +56,7 @@ struct RowState {
   float l_run;   // this lane's half of the row sum
   int koff[kBf ? kQSteps : 1];
   int voff[kBf ? 2 * kDB : 1];
-  int h, n, row, ra, rb;
+  int h, n, lane_id, row, ra, rb;
   uint64_t rmask;
   bool row_ok;
   float c, tau;  // scale * log2(e); fp32: base move threshold
@@ -152,11 +152,13 @@ struct RowState {
       }
       u32x4 pw[2][2];
       float ls = exp_pack(s, pw);
-      // the decision is the row's own (both lanes of a row see the same
-      // pair maximum); __any only skips the branch when no row needs it
-      const bool over = pair_max(ls) > 65536.f;
-      if (__any(over)) {
-        rebase(s, over);
+      // the decision is the row's own: a row is over when either of its two
+      // lanes is (the same as its pair maximum passing 2^16); the common
+      // path pays one compare and a scalar test of the wave's lane mask
+      const uint64_t lanes_over = __ballot(ls > 65536.f);
+      if (lanes_over) {
+        const uint64_t rows_over = lanes_over | (lanes_over >> 32) | (lanes_over << 32);
+        rebase(s, ((rows_over >> lane_id) & 1u) != 0);
         ls = exp_pack(s, pw);
       }
       l_run += ls;
@@ -352,6 +354,7 @@ __global__ __launch_bounds__(128 * GH, 2) void attn_kernel(AttnParams p) {
   RS rs;
   rs.h = lane >> 5;
   rs.n = lane & 31;
+  rs.lane_id = lane;
   const int tok = wave * TPW + rs.n / GH;
   const int head = kvh * p.group + int(blockIdx.y) * GH + (rs.n % GH);
   rs.row_ok = tok < wi.nrows;
