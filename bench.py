@@ -448,7 +448,20 @@ def calibrate():
     rsink = torch.empty(32768, dtype=torch.int32, device="cuda")
     read = {blocks: timed(lambda: ta.calib_read(src, blocks, rsink)) / 1e9 for blocks in (2048, 4096, 8192, 16384, 32768)}
     del src
+    # the attention tile loop's own instruction mix (a model of the forward's
+    # 64-key tile: 32 MFMAs and the softmax per wave and iteration): with
+    # register operands, LDS operands, and LDS operands plus the per-tile copy
+    tsrc = torch.ones(16 << 20, dtype=torch.uint8, device="cuda")
+    tile = {v: max(timed(lambda: ta.calib_tile(v, blocks, 2000, sink, tsrc)) / 1e12 for blocks in (512, 1024))
+            for v in (0, 1, 2)}
+    del tsrc
     return {"mfma_bf16_tflops": max(mfma.values()), "hbm_read_gbs": max(read.values()),
+            "tile_loop_tflops": {"registers": tile[0], "lds_operands": tile[1], "lds_operands_and_copy": tile[2]},
+            "tile_loop": "tree_attn_calib_tile: the forward's 64-key tile loop at bf16 / head_dim 128 (16 S "
+                         "MFMAs, the softmax of 32 scores and its 2^16 test, 16 PV MFMAs, a barrier per "
+                         "iteration), 2,000 iterations, best of 512/1024 workgroups of 4 waves; operands from "
+                         "registers / from an LDS tile in the kernel's layout / the same plus the kernel's "
+                         "copy of the next tile per iteration (16 MiB source, L2-resident per KV head)",
             "mfma_loop": "tree_attn_calib_mfma: waves issuing back-to-back bf16 32x32x16 MFMAs on 8 accumulators, "
                          "4,000 rounds; best of 1024/2048/4096 workgroups of 4 waves: "
                          + ", ".join(f"{k}: {v:.0f}" for k, v in mfma.items()) + " TFLOP/s",
@@ -499,7 +512,9 @@ def main():
     if not args.no_calib and args.only is None:
         attainable = calibrate()
         log(f"[bench] attainable: {attainable['mfma_bf16_tflops']:.0f} TFLOP/s bf16, "
-            f"{attainable['hbm_read_gbs']:.0f} GB/s read")
+            f"{attainable['hbm_read_gbs']:.0f} GB/s read; tile-loop model "
+            + " / ".join(f"{v:.0f}" for v in attainable["tile_loop_tflops"].values())
+            + " TFLOP/s (registers / LDS operands / LDS operands + copy)")
     log("[bench] generating inputs")
     cases = []
     for name, fn in ENTRIES.items():
@@ -541,6 +556,9 @@ def main():
         if attainable:
             r["flop_frac_attainable"] = tflops / attainable["mfma_bf16_tflops"]
             r["byte_frac_attainable"] = gbs / attainable["hbm_read_gbs"]
+            if c["name"] in ("prefill", "verify", "prefill_1page"):
+                # against the model of the forward's own tile loop with its copies
+                r["flop_frac_tile_model"] = tflops / attainable["tile_loop_tflops"]["lds_operands_and_copy"]
         if c["bound"] == "mfma":
             r["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                              "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic_for(c["name"])}

@@ -483,7 +483,7 @@ const char* tree_attn_version(void);
 
 /* ---- Roofline calibration (measurement only; not part of the attention
  * path).  Attention kernels are reported against MI355X's published peaks
- * (2.5 PFLOP/s dense bf16, 8 TB/s HBM3E) and against what these two loops
+ * (2.5 PFLOP/s dense bf16, 8 TB/s HBM3E) and against what these loops
  * reach on the GPU at hand under load. */
 
 /* Enqueue `blocks` workgroups of 4 waves, each wave issuing `iters` rounds of
@@ -500,6 +500,24 @@ int tree_attn_calib_mfma(int32_t blocks, int32_t iters, float* sink, int64_t* fl
  * written to sink (device, >= blocks uint32).  Errors: INVALID_ARG as for
  * tree_attn_calib_mfma. */
 int tree_attn_calib_read(const void* src, int64_t bytes, int32_t blocks, uint32_t* sink, void* stream);
+
+/* Enqueue a model of the attention kernel's 64-key tile loop (bf16,
+ * head_dim 128; PaDoc summary, "Training paradigm": the causal attention
+ * the forward computes per tile): `blocks` workgroups of 4 waves, each wave
+ * running `iters` iterations of 16 S MFMAs, the online-softmax vector work of
+ * 32 scores (exp2 arguments, exponentials, bf16 packing, row sums, the 2^16
+ * test that gates the PV step) and 16 PV MFMAs, with a workgroup barrier per
+ * iteration.  variant 0: K and V operands held in registers; 1: read from an
+ * LDS tile in the kernel's layout; 2: as 1, and every iteration also copies
+ * the next 64-key K/V tile from src (device, 16-byte aligned, >= 262,144
+ * bytes: K rows in the first half, V rows in the second, 2,048-byte rows)
+ * into a second LDS stage.  *flops receives the launch's MFMA FLOPs
+ * (32,768 per MFMA).  sink: device, >= 4 * blocks floats (written, contents
+ * meaningless).  Errors: INVALID_ARG for a variant outside [0, 2], blocks or
+ * iters out of range as for tree_attn_calib_mfma, or a NULL / misaligned /
+ * short argument. */
+int tree_attn_calib_tile(int32_t variant, int32_t blocks, int32_t iters, const void* src, int64_t src_bytes,
+                         float* sink, int64_t* flops, void* stream);
 
 #ifdef __cplusplus
 }

@@ -208,3 +208,18 @@ def test_decode_noalloc_host_checks():
     rc = L.tree_attn_decode_noalloc(small.handle, ta.TA_DTYPE_BF16, 16, 8, 128, 0.088, fake, fake, fake, fake,
                                     fake, fake, None, None)
     assert rc == ta.TA_ERR_STATE
+
+
+def test_calib_tile_host_checks():
+    """tree_attn_calib_tile rejects a bad variant, a missing or short copy
+    source (variant 2) and out-of-range sizes on the host, before any launch
+    (a fake, never dereferenced pointer stands in for the sink)."""
+    import ctypes
+    L = ta.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    flops = ctypes.c_int64()
+    for args in ((3, 8, 5, None, 0), (-1, 8, 5, None, 0), (2, 8, 5, None, 0), (2, 8, 5, fake, 4096),
+                 (0, 0, 5, None, 0), (0, 8, 0, None, 0)):
+        rc = L.tree_attn_calib_tile(*args, fake, ctypes.byref(flops), None)
+        assert rc == ta.TA_ERR_INVALID_ARG, (args, rc)
+        assert "calib_tile" in ta.last_error()

@@ -141,6 +141,7 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int),
             "tree_attn_calib_mfma": ([i32, i32, _P, _I64P, _P], ctypes.c_int),
             "tree_attn_calib_read": ([_P, i64, i32, _P, _P], ctypes.c_int),
+            "tree_attn_calib_tile": ([i32, i32, i32, _P, i64, _P, _I64P, _P], ctypes.c_int),
             "tree_attn_last_error": ([], ctypes.c_char_p),
             "tree_attn_version": ([], ctypes.c_char_p),
         }
@@ -767,3 +768,20 @@ def calib_read(src: torch.Tensor, blocks: int, sink: torch.Tensor, stream=None) 
     nbytes = src.numel() * src.element_size()
     _check(lib().tree_attn_calib_read(_dev_ptr(src), nbytes, int(blocks), _dev_ptr(sink), _stream_handle(stream)))
     return nbytes
+
+
+def calib_tile(variant: int, blocks: int, iters: int, sink: torch.Tensor, src: torch.Tensor = None,
+               stream=None) -> int:
+    """Enqueue the tile-loop model (variant 0: register operands, 1: LDS
+    operands, 2: LDS operands and a copy per iteration from src); returns its
+    MFMA FLOP count.  sink: float32 tensor of >= 4 * blocks entries on the
+    GPU; src (variant 2): a GPU tensor of >= 262,144 bytes."""
+    if sink.dtype != torch.float32 or sink.numel() < 4 * blocks:
+        raise _bad("sink must be float32 with at least 4 * blocks entries")
+    sp, nbytes = None, 0
+    if src is not None:
+        sp, nbytes = _dev_ptr(src), src.numel() * src.element_size()
+    flops = ctypes.c_int64()
+    _check(lib().tree_attn_calib_tile(int(variant), int(blocks), int(iters), sp, nbytes, _dev_ptr(sink),
+                                      ctypes.byref(flops), _stream_handle(stream)))
+    return int(flops.value)
