@@ -62,7 +62,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
-@pytest.mark.parametrize("heads", [(16, 8, 128), (8, 8, 64), (8, 2, 32), (4, 1, 128)])
+@pytest.mark.parametrize("heads", [(16, 8, 128), (8, 8, 64), (8, 2, 32), (4, 1, 128), (32, 1, 64)])
 def test_backward_small(case, heads):
     hq, hkv, d = heads
     desc, t, g = make(CASES[case], hq, hkv, d, seed=31 * case + d)

@@ -141,3 +141,44 @@ def test_verify_random_description(seed):
     ro, rl = oracle.verify(desc, t["q"], t["k_ctx"], t["v_ctx"], t["k_tree"], t["v_tree"], d ** -0.5)
     close(o.float().cpu().numpy(), ro, TOL[dtype][0], "o")
     close(lse.cpu().numpy(), rl, TOL[dtype][1], "lse")
+
+
+@pytest.mark.parametrize("entry", ["prefill", "decode", "verify"])
+def test_largest_head_group(entry):
+    """32 query heads on one KV head (the largest group the library takes):
+    sixteen head pairs per KV head, every entry point against the oracle."""
+    hq, hkv, d, dtype = 32, 1, 64, torch.bfloat16
+    rng = np.random.default_rng(4242)
+    print(f"[sweep] group 32 {entry}", flush=True)
+    if entry == "prefill":
+        desc = synth.make_prefill_desc([130, 7], [np.array([2, 1]), np.array([1])], [np.array([65, 3]), np.array([64])])
+        t = synth.prefill_tensors(rng, desc, hq, hkv, d, dtype)
+        plan = ta.plan_for(desc).upload()
+        g = {k: v.cuda() for k, v in t.items()}
+        o, lse = ta.prefill(plan, g["q"], g["k"], g["v"], scale=d ** -0.5)
+        torch.cuda.synchronize()
+        ro, rl = oracle.prefill(desc, t["q"], t["k"], t["v"], d ** -0.5)
+    elif entry == "decode":
+        desc = synth.DecodeDesc(np.array([150, 64], np.int32), np.array([2, 1], np.int32),
+                                np.array([4, 12, 0], np.int32), np.array([0, 0, 1], np.int32),
+                                np.array([1, 2, 0], np.int32), np.array([3, 70, 0], np.int32),
+                                np.array([1, 8, 2], np.int32))
+        t = synth.decode_tensors(rng, desc, hq, hkv, d, dtype)
+        plan = ta.plan_for(desc).upload()
+        g = {k: v.cuda() for k, v in t.items()}
+        o, lse = ta.decode(plan, g["q"], g["k_main"], g["v_main"], g["k_suffix"], g["v_suffix"], scale=d ** -0.5)
+        torch.cuda.synchronize()
+        ro, rl = oracle.decode(desc, t["q"], t["k_main"], t["v_main"], t["k_suffix"], t["v_suffix"], d ** -0.5)
+    else:
+        par = synth.random_tree_parents(rng, 20).astype(np.int32)
+        desc = synth.VerifyDesc(np.array([100, 65], np.int32), np.array([0, 1, 1], np.int32),
+                                np.array([20, 1, 3], np.int32),
+                                np.concatenate([par, np.array([-1, -1, 0, 1], np.int32)]))
+        t = synth.verify_tensors(rng, desc, hq, hkv, d, dtype)
+        plan = ta.plan_for(desc).upload()
+        g = {k: v.cuda() for k, v in t.items()}
+        o, lse = ta.verify(plan, g["q"], g["k_ctx"], g["v_ctx"], g["k_tree"], g["v_tree"], scale=d ** -0.5)
+        torch.cuda.synchronize()
+        ro, rl = oracle.verify(desc, t["q"], t["k_ctx"], t["v_ctx"], t["k_tree"], t["v_tree"], d ** -0.5)
+    close(o.float().cpu().numpy(), ro, TOL[dtype][0], "o")
+    close(lse.cpu().numpy(), rl, TOL[dtype][1], "lse")
