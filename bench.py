@@ -64,6 +64,10 @@ def scratch_for(plan, w):
     return torch.empty(n + 256, dtype=torch.uint8, device="cuda") if n else None
 
 
+# --zero-inputs (diagnostic): the prefill entries run on all-zero q / k / v
+ZERO_INPUTS = False
+
+
 def prefill_case(w=None, name="prefill", in_step=True):
     """Packed prefill over a balanced plan (row tiles split so the launch
     fills the chip); the host plan's steady-state cost is timed on a second
@@ -75,6 +79,9 @@ def prefill_case(w=None, name="prefill", in_step=True):
     plan_us = (time.perf_counter() - t0) * 1e6
     plan.upload()
     t = {k: v.cuda() for k, v in w.tensors.items()}
+    if ZERO_INPUTS:
+        for x in t.values():
+            x.zero_()
     o = torch.empty_like(t["q"])
     lse = torch.empty((w.hq, t["q"].shape[0]), dtype=torch.float32, device="cuda")
     scratch = scratch_for(plan, w)
@@ -443,28 +450,46 @@ def calibrate():
         return best
 
     sink = torch.empty(4 * 4096, dtype=torch.float32, device="cuda")
-    mfma = {blocks: timed(lambda: ta.calib_mfma(blocks, 4000, sink)) / 1e12 for blocks in (1024, 2048, 4096)}
+    # matrix-core loops twice: pseudo-random operands that differ from one
+    # instruction to the next (as the attention kernels' operands do on
+    # N(0,1) data), then one fixed operand pattern; the chip lowers its clock
+    # under the power limit on the first kind
+    seed = 0x5EED
+    mfma = {blocks: timed(lambda: ta.calib_mfma(blocks, 4000, sink, seed=seed)) / 1e12 for blocks in (1024, 2048, 4096)}
+    mfma_fixed = {blocks: timed(lambda: ta.calib_mfma(blocks, 4000, sink)) / 1e12 for blocks in (1024, 2048, 4096)}
     src = torch.ones(1 << 32, dtype=torch.uint8, device="cuda")  # 4 GiB
     rsink = torch.empty(32768, dtype=torch.int32, device="cuda")
     read = {blocks: timed(lambda: ta.calib_read(src, blocks, rsink)) / 1e9 for blocks in (2048, 4096, 8192, 16384, 32768)}
     del src
     # the attention tile loop's own instruction mix (a model of the forward's
     # 64-key tile: 32 MFMAs and the softmax per wave and iteration): with
-    # register operands, LDS operands, and LDS operands plus the per-tile copy
-    tsrc = torch.ones(16 << 20, dtype=torch.uint8, device="cuda")
-    tile = {v: max(timed(lambda: ta.calib_tile(v, blocks, 2000, sink, tsrc)) / 1e12 for blocks in (512, 1024))
-            for v in (0, 1, 2)}
-    del tsrc
+    # register operands, LDS operands, and LDS operands plus the per-tile
+    # copy; random Q / K / V (N(0,1) bf16 copy source), then fixed patterns
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    tsrc = torch.randn(8 << 20, dtype=torch.bfloat16, device="cuda", generator=gen)  # 16 MiB
+    tsrc_fixed = torch.ones(16 << 20, dtype=torch.uint8, device="cuda")
+    names = ("registers", "lds_operands", "lds_operands_and_copy")
+    tile = {names[v]: max(timed(lambda: ta.calib_tile(v, blocks, 2000, sink, tsrc, seed=seed)) / 1e12
+                          for blocks in (512, 1024)) for v in (0, 1, 2)}
+    tile_fixed = {names[v]: max(timed(lambda: ta.calib_tile(v, blocks, 2000, sink, tsrc_fixed)) / 1e12
+                                for blocks in (512, 1024)) for v in (0, 1, 2)}
+    del tsrc, tsrc_fixed
     return {"mfma_bf16_tflops": max(mfma.values()), "hbm_read_gbs": max(read.values()),
-            "tile_loop_tflops": {"registers": tile[0], "lds_operands": tile[1], "lds_operands_and_copy": tile[2]},
+            "tile_loop_tflops": tile,
+            "fixed_operands": {"mfma_bf16_tflops": max(mfma_fixed.values()), "tile_loop_tflops": tile_fixed},
             "tile_loop": "tree_attn_calib_tile: the forward's 64-key tile loop at bf16 / head_dim 128 (16 S "
                          "MFMAs, the softmax of 32 scores and its 2^16 test, 16 PV MFMAs, a barrier per "
                          "iteration), 2,000 iterations, best of 512/1024 workgroups of 4 waves; operands from "
                          "registers / from an LDS tile in the kernel's layout / the same plus the kernel's "
-                         "copy of the next tile per iteration (16 MiB source, L2-resident per KV head)",
+                         "copy of the next tile per iteration (16 MiB source, L2-resident per KV head); "
+                         "pseudo-random Q, K, V (N(0,1) bf16 source); 'fixed_operands': the same loops on fixed "
+                         "operand patterns",
             "mfma_loop": "tree_attn_calib_mfma: waves issuing back-to-back bf16 32x32x16 MFMAs on 8 accumulators, "
-                         "4,000 rounds; best of 1024/2048/4096 workgroups of 4 waves: "
-                         + ", ".join(f"{k}: {v:.0f}" for k, v in mfma.items()) + " TFLOP/s",
+                         "4,000 rounds; best of 1024/2048/4096 workgroups of 4 waves; pseudo-random operands, a "
+                         "different pair per accumulator: "
+                         + ", ".join(f"{k}: {v:.0f}" for k, v in mfma.items()) + " TFLOP/s; one fixed operand "
+                         "pair ('fixed_operands'): " + ", ".join(f"{k}: {v:.0f}" for k, v in mfma_fixed.items())
+                         + " TFLOP/s",
             "read_loop": "tree_attn_calib_read: 4 GiB streamed with 16-byte non-temporal loads; best of "
                          "2048-32768 workgroups of 256 threads: "
                          + ", ".join(f"{k}: {v:.0f}" for k, v in read.items()) + " GB/s"}
@@ -491,7 +516,16 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB three times "
                          "(reference for scaling HBM byte counters)")
+    ap.add_argument("--zero-inputs", action="store_true",
+                    help="diagnostic: run the prefill entry chosen by --only on all-zero q, k, v (the same "
+                         "instructions with no bit activity in the data; compare with the default run)")
     args = ap.parse_args()
+    if args.zero_inputs:
+        if args.only not in ("prefill", "prefill_1page"):
+            print("--zero-inputs needs --only prefill or --only prefill_1page", file=sys.stderr)
+            sys.exit(2)
+        global ZERO_INPUTS
+        ZERO_INPUTS = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the tree attention path has no multi-GPU mode "
               "(pages shard across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
@@ -511,9 +545,12 @@ def main():
     attainable = None
     if not args.no_calib and args.only is None:
         attainable = calibrate()
-        log(f"[bench] attainable: {attainable['mfma_bf16_tflops']:.0f} TFLOP/s bf16, "
+        log(f"[bench] attainable: {attainable['mfma_bf16_tflops']:.0f} TFLOP/s bf16 "
+            f"({attainable['fixed_operands']['mfma_bf16_tflops']:.0f} on fixed operands), "
             f"{attainable['hbm_read_gbs']:.0f} GB/s read; tile-loop model "
             + " / ".join(f"{v:.0f}" for v in attainable["tile_loop_tflops"].values())
+            + " (fixed operands: "
+            + " / ".join(f"{v:.0f}" for v in attainable["fixed_operands"]["tile_loop_tflops"].values()) + ")"
             + " TFLOP/s (registers / LDS operands / LDS operands + copy)")
     log("[bench] generating inputs")
     cases = []
@@ -585,7 +622,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "zeros (diagnostic)" if ZERO_INPUTS else "synthetic",
         "config": {"workload": "packed tree-varlen prefill, batch of 8 pages (seed 2): P=4096, N~U{12..40} regions, "
                                "L=12, lognormal content clipped to [8,1024], cap 16,384 per page, 77,400 packed "
                                "tokens; 16q/8kv heads, d=128, bf16. Step also runs decode (16 pages x 24 branches, "

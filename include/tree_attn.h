@@ -488,11 +488,15 @@ const char* tree_attn_version(void);
 
 /* Enqueue `blocks` workgroups of 4 waves, each wave issuing `iters` rounds of
  * 8 independent bf16 32x32x16 MFMAs from registers (no memory traffic in the
- * loop).  *flops receives the launch's FLOP count (32,768 per MFMA); time
- * the launch with events on `stream`.  sink: device, >= 4 * blocks floats
- * (written, contents meaningless).  Errors: INVALID_ARG for blocks outside
- * [1, 2^20], iters outside [1, 2^24] or a NULL / misaligned pointer. */
-int tree_attn_calib_mfma(int32_t blocks, int32_t iters, float* sink, int64_t* flops, void* stream);
+ * loop).  seed 0: one fixed operand pair, the same bits in every
+ * instruction; any other seed: a pseudo-random operand pair per accumulator
+ * (random sign and mantissa), so that consecutive instructions differ as on
+ * real data (the chip draws more power then and clocks lower).  *flops
+ * receives the launch's FLOP count (32,768 per MFMA); time the launch with
+ * events on `stream`.  sink: device, >= 4 * blocks floats (written, contents
+ * meaningless).  Errors: INVALID_ARG for blocks outside [1, 2^20], iters
+ * outside [1, 2^24] or a NULL / misaligned pointer. */
+int tree_attn_calib_mfma(int32_t blocks, int32_t iters, uint32_t seed, float* sink, int64_t* flops, void* stream);
 
 /* Enqueue a streaming read of `bytes` (a positive multiple of 16) at src
  * (device, 16-byte aligned): `blocks` workgroups of 256 threads, 16-byte
@@ -511,13 +515,15 @@ int tree_attn_calib_read(const void* src, int64_t bytes, int32_t blocks, uint32_
  * LDS tile in the kernel's layout; 2: as 1, and every iteration also copies
  * the next 64-key K/V tile from src (device, 16-byte aligned, >= 262,144
  * bytes: K rows in the first half, V rows in the second, 2,048-byte rows)
- * into a second LDS stage.  *flops receives the launch's MFMA FLOPs
- * (32,768 per MFMA).  sink: device, >= 4 * blocks floats (written, contents
- * meaningless).  Errors: INVALID_ARG for a variant outside [0, 2], blocks or
- * iters out of range as for tree_attn_calib_mfma, or a NULL / misaligned /
- * short argument. */
-int tree_attn_calib_tile(int32_t variant, int32_t blocks, int32_t iters, const void* src, int64_t src_bytes,
-                         float* sink, int64_t* flops, void* stream);
+ * into a second LDS stage.  seed 0: fixed, slowly varying register and LDS
+ * operands; any other seed: pseudo-random bf16 Q, K and V in registers and
+ * in the variant-1 LDS tile (variant 2 copies whatever src holds).  *flops
+ * receives the launch's MFMA FLOPs (32,768 per MFMA).  sink: device,
+ * >= 4 * blocks floats (written, contents meaningless).  Errors: INVALID_ARG
+ * for a variant outside [0, 2], blocks or iters out of range as for
+ * tree_attn_calib_mfma, or a NULL / misaligned / short argument. */
+int tree_attn_calib_tile(int32_t variant, int32_t blocks, int32_t iters, uint32_t seed, const void* src,
+                         int64_t src_bytes, float* sink, int64_t* flops, void* stream);
 
 #ifdef __cplusplus
 }

@@ -218,8 +218,12 @@ def test_calib_tile_host_checks():
     L = ta.lib()
     fake = ctypes.c_void_p(1 << 20)
     flops = ctypes.c_int64()
-    for args in ((3, 8, 5, None, 0), (-1, 8, 5, None, 0), (2, 8, 5, None, 0), (2, 8, 5, fake, 4096),
-                 (0, 0, 5, None, 0), (0, 8, 0, None, 0)):
+    for args in ((3, 8, 5, 0, None, 0), (-1, 8, 5, 7, None, 0), (2, 8, 5, 0, None, 0), (2, 8, 5, 7, fake, 4096),
+                 (0, 0, 5, 0, None, 0), (0, 8, 0, 7, None, 0)):
         rc = L.tree_attn_calib_tile(*args, fake, ctypes.byref(flops), None)
         assert rc == ta.TA_ERR_INVALID_ARG, (args, rc)
         assert "calib_tile" in ta.last_error()
+    for args in ((0, 5, 0), (8, 0, 7), (1 << 21, 5, 0)):
+        rc = L.tree_attn_calib_mfma(*args, fake, ctypes.byref(flops), None)
+        assert rc == ta.TA_ERR_INVALID_ARG, (args, rc)
+        assert "calib_mfma" in ta.last_error()

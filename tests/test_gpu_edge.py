@@ -88,17 +88,20 @@ def test_calibration_loops_do_their_work():
         torch.cuda.synchronize()
         got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
         assert got == np.bitwise_xor.reduce(words.view(np.uint32)), n_words
-    fsink = torch.zeros(4 * 8, dtype=torch.float32, device="cuda")
-    assert ta.calib_mfma(8, 10, fsink) == 8 * 4 * 10 * 8 * 32768
-    torch.cuda.synchronize()
-    assert torch.isfinite(fsink).all() and (fsink != 0).all()
+    for seed in (0, 7):  # fixed operands, then pseudo-random ones
+        fsink = torch.zeros(4 * 8, dtype=torch.float32, device="cuda")
+        assert ta.calib_mfma(8, 10, fsink, seed=seed) == 8 * 4 * 10 * 8 * 32768
+        torch.cuda.synchronize()
+        assert torch.isfinite(fsink).all() and (fsink != 0).all(), seed
     with pytest.raises(ta.TreeAttnError):
         ta.calib_read(src[:3], 4, sink)  # 12 bytes: not a multiple of 16
     # the tile-loop model, each variant: 32 MFMAs of 32,768 FLOP per wave and
     # iteration, every wave writes a finite word
     tile_src = torch.ones(1 << 20, dtype=torch.uint8, device="cuda")
     for variant in (0, 1, 2):
-        fsink = torch.full((4 * 8,), float("nan"), dtype=torch.float32, device="cuda")
-        assert ta.calib_tile(variant, 8, 5, fsink, tile_src if variant == 2 else None) == 8 * 4 * 5 * 32 * 32768
-        torch.cuda.synchronize()
-        assert torch.isfinite(fsink).all(), variant
+        for seed in (0, 7):
+            fsink = torch.full((4 * 8,), float("nan"), dtype=torch.float32, device="cuda")
+            src = tile_src if variant == 2 else None
+            assert ta.calib_tile(variant, 8, 5, fsink, src, seed=seed) == 8 * 4 * 5 * 32 * 32768
+            torch.cuda.synchronize()
+            assert torch.isfinite(fsink).all(), (variant, seed)

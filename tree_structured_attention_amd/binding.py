@@ -139,9 +139,9 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_int),
             "tree_attn_decode_noalloc": ([_P, i32, i32, i32, i32, f32, _P, _P, _P, _P, _P, _P, _P, _P],
                                          ctypes.c_int),
-            "tree_attn_calib_mfma": ([i32, i32, _P, _I64P, _P], ctypes.c_int),
+            "tree_attn_calib_mfma": ([i32, i32, ctypes.c_uint32, _P, _I64P, _P], ctypes.c_int),
             "tree_attn_calib_read": ([_P, i64, i32, _P, _P], ctypes.c_int),
-            "tree_attn_calib_tile": ([i32, i32, i32, _P, i64, _P, _I64P, _P], ctypes.c_int),
+            "tree_attn_calib_tile": ([i32, i32, i32, ctypes.c_uint32, _P, i64, _P, _I64P, _P], ctypes.c_int),
             "tree_attn_last_error": ([], ctypes.c_char_p),
             "tree_attn_version": ([], ctypes.c_char_p),
         }
@@ -749,13 +749,15 @@ class KVPool:
 # roofline calibration (measurement only)
 # ---------------------------------------------------------------------------
 
-def calib_mfma(blocks: int, iters: int, sink: torch.Tensor, stream=None) -> int:
-    """Enqueue the bf16 MFMA loop; returns its FLOP count.  sink: float32
-    tensor of >= 4 * blocks entries on the GPU."""
+def calib_mfma(blocks: int, iters: int, sink: torch.Tensor, seed: int = 0, stream=None) -> int:
+    """Enqueue the bf16 MFMA loop (seed 0: one fixed operand pair; otherwise
+    pseudo-random operands that differ between instructions); returns its
+    FLOP count.  sink: float32 tensor of >= 4 * blocks entries on the GPU."""
     if sink.dtype != torch.float32 or sink.numel() < 4 * blocks:
         raise _bad("sink must be float32 with at least 4 * blocks entries")
     flops = ctypes.c_int64()
-    _check(lib().tree_attn_calib_mfma(int(blocks), int(iters), _dev_ptr(sink), ctypes.byref(flops),
+    _check(lib().tree_attn_calib_mfma(int(blocks), int(iters), int(seed) & 0xFFFFFFFF, _dev_ptr(sink),
+                                      ctypes.byref(flops),
                                       _stream_handle(stream)))
     return int(flops.value)
 
@@ -771,17 +773,18 @@ def calib_read(src: torch.Tensor, blocks: int, sink: torch.Tensor, stream=None) 
 
 
 def calib_tile(variant: int, blocks: int, iters: int, sink: torch.Tensor, src: torch.Tensor = None,
-               stream=None) -> int:
+               seed: int = 0, stream=None) -> int:
     """Enqueue the tile-loop model (variant 0: register operands, 1: LDS
-    operands, 2: LDS operands and a copy per iteration from src); returns its
-    MFMA FLOP count.  sink: float32 tensor of >= 4 * blocks entries on the
-    GPU; src (variant 2): a GPU tensor of >= 262,144 bytes."""
+    operands, 2: LDS operands and a copy per iteration from src; seed 0:
+    fixed operand patterns, otherwise pseudo-random ones); returns its MFMA
+    FLOP count.  sink: float32 tensor of >= 4 * blocks entries on the GPU;
+    src (variant 2): a GPU tensor of >= 262,144 bytes."""
     if sink.dtype != torch.float32 or sink.numel() < 4 * blocks:
         raise _bad("sink must be float32 with at least 4 * blocks entries")
     sp, nbytes = None, 0
     if src is not None:
         sp, nbytes = _dev_ptr(src), src.numel() * src.element_size()
     flops = ctypes.c_int64()
-    _check(lib().tree_attn_calib_tile(int(variant), int(blocks), int(iters), sp, nbytes, _dev_ptr(sink),
-                                      ctypes.byref(flops), _stream_handle(stream)))
+    _check(lib().tree_attn_calib_tile(int(variant), int(blocks), int(iters), int(seed) & 0xFFFFFFFF, sp, nbytes,
+                                      _dev_ptr(sink), ctypes.byref(flops), _stream_handle(stream)))
     return int(flops.value)

@@ -534,12 +534,13 @@ extern "C" int tree_attn_accept(const ta_plan* plan, int32_t dtype, const void* 
   return ta::fail_exception("accept");
 }
 
-extern "C" int tree_attn_calib_mfma(int32_t blocks, int32_t iters, float* sink, int64_t* flops, void* stream) try {
+extern "C" int tree_attn_calib_mfma(int32_t blocks, int32_t iters, uint32_t seed, float* sink, int64_t* flops,
+                                    void* stream) try {
   if (blocks <= 0 || blocks > (1 << 20) || iters <= 0 || iters > (1 << 24))
     return fail(TA_ERR_INVALID_ARG, "calib_mfma: blocks must be in [1, 2^20] and iters in [1, 2^24]");
   if (!sink || !aligned(sink, 4) || !flops) return fail(TA_ERR_INVALID_ARG, "calib_mfma: NULL or misaligned argument");
   *flops = calib_mfma_flops(blocks, iters);
-  return hip_status(launch_calib_mfma(blocks, iters, sink, static_cast<hipStream_t>(stream)), "calib_mfma launch");
+  return hip_status(launch_calib_mfma(blocks, iters, seed, sink, static_cast<hipStream_t>(stream)), "calib_mfma launch");
 } catch (...) {
   return ta::fail_exception("calib_mfma");
 }
@@ -555,7 +556,7 @@ extern "C" int tree_attn_calib_read(const void* src, int64_t bytes, int32_t bloc
   return ta::fail_exception("calib_read");
 }
 
-extern "C" int tree_attn_calib_tile(int32_t variant, int32_t blocks, int32_t iters, const void* src,
+extern "C" int tree_attn_calib_tile(int32_t variant, int32_t blocks, int32_t iters, uint32_t seed, const void* src,
                                     int64_t src_bytes, float* sink, int64_t* flops, void* stream) try {
   if (variant < 0 || variant > 2) return fail(TA_ERR_INVALID_ARG, "calib_tile: variant must be 0, 1 or 2");
   if (blocks <= 0 || blocks > (1 << 20) || iters <= 0 || iters > (1 << 24))
@@ -565,7 +566,8 @@ extern "C" int tree_attn_calib_tile(int32_t variant, int32_t blocks, int32_t ite
     return fail(TA_ERR_INVALID_ARG, "calib_tile: variant 2 needs a 16-byte aligned src of at least " +
                                         std::to_string(calib_tile_min_bytes()) + " bytes");
   *flops = calib_tile_flops(blocks, iters);
-  return hip_status(launch_calib_tile(variant, blocks, iters, src, src_bytes, sink, static_cast<hipStream_t>(stream)),
+  return hip_status(launch_calib_tile(variant, blocks, iters, seed, src, src_bytes, sink,
+                                      static_cast<hipStream_t>(stream)),
                     "calib_tile launch");
 } catch (...) {
   return ta::fail_exception("calib_tile");

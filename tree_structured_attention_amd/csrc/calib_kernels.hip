@@ -23,6 +23,12 @@
 //                       iteration, as the kernel does.  The rates bound what
 //                       the tile loop can reach with and without each of the
 //                       kernel's memory steps.
+// The matrix-core loops take a seed: 0 keeps one fixed, slowly varying
+// operand pattern (few bits change from one instruction to the next); any
+// other seed fills the operands with pseudo-random bf16 values, so that
+// consecutive instructions see unrelated bits as the attention kernels do on
+// real data.  The chip draws more power on the second kind and lowers its
+// clock under the power limit, so the two rates differ.
 #include <algorithm>
 
 #include "ta_device.h"
@@ -33,14 +39,37 @@ namespace {
 constexpr int kCalibThreads = 256;
 constexpr int kCalibAcc = 8;
 
-__global__ __launch_bounds__(kCalibThreads) void calib_mfma_kernel(int32_t iters, float* sink) {
+// MurmurHash3's 32-bit finalizer (Appleby): a counter-based source of
+// well-mixed bits.
+__device__ __forceinline__ uint32_t fmix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x85ebca6bu;
+  x ^= x >> 13;
+  x *= 0xc2b2ae35u;
+  x ^= x >> 16;
+  return x;
+}
+// A pseudo-random bf16 of element `i` under `seed`: random sign and
+// mantissa, magnitude in [2^-4, 1).
+__device__ __forceinline__ __bf16 rand_bf16(uint32_t seed, uint32_t i) {
+  const uint32_t h = fmix32(fmix32(seed) ^ (i * 0x9e3779b9u));
+  return __builtin_bit_cast(__bf16, uint16_t((h & 0x807fu) | ((123u + ((h >> 8) & 3u)) << 7)));
+}
+__device__ __forceinline__ uint32_t thread_id() { return blockIdx.x * blockDim.x + threadIdx.x; }
+
+__global__ __launch_bounds__(kCalibThreads) void calib_mfma_kernel(int32_t iters, uint32_t seed, float* sink) {
   const int lane = threadIdx.x & 63;
-  bf16x8 a, b;
+  // seed 0: one operand pair for every instruction; otherwise a random pair
+  // per accumulator, so consecutive instructions differ in every operand
+  bf16x8 a[kCalibAcc], b[kCalibAcc];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a[e] = static_cast<__bf16>(1e-3f * float(lane + e));
-    b[e] = static_cast<__bf16>(1e-3f * float(64 - lane + e));
-  }
+  for (int j = 0; j < kCalibAcc; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t i = (thread_id() * kCalibAcc + j) * 16 + e;
+      a[j][e] = seed ? rand_bf16(seed, i) : static_cast<__bf16>(1e-3f * float(lane + e));
+      b[j][e] = seed ? rand_bf16(seed, i + 8) : static_cast<__bf16>(1e-3f * float(64 - lane + e));
+    }
   f32x16 acc[kCalibAcc];
 #pragma unroll
   for (int j = 0; j < kCalibAcc; ++j)
@@ -48,7 +77,7 @@ __global__ __launch_bounds__(kCalibThreads) void calib_mfma_kernel(int32_t iters
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
   for (int32_t i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int j = 0; j < kCalibAcc; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    for (int j = 0; j < kCalibAcc; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[j], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
@@ -91,25 +120,28 @@ constexpr int kTileD = 128;
 constexpr int64_t kTileRowStride = 8 * kTileD * 2;  // 8 KV heads of bf16 per key row
 
 template <int VAR>
-__global__ __launch_bounds__(256, 2) void calib_tile_kernel(int32_t iters, float* sink, const unsigned char* src,
-                                                            int32_t n_tiles) {
+__global__ __launch_bounds__(256, 2) void calib_tile_kernel(int32_t iters, uint32_t seed, float* sink,
+                                                            const unsigned char* src, int32_t n_tiles) {
   using G = TileGeom<__bf16, kTileD>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[VAR == 0 ? 16 : (VAR == 1 ? 1 : 2) * G::kStageBytes];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int n = lane & 31, h = lane >> 5;
   bf16x8 qf[8], kf[8], kg[8], vf[4];
+  const uint32_t r0 = thread_id() * 224;  // 224 register operands per lane
 #pragma unroll
   for (int st = 0; st < 8; ++st)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      qf[st][e] = static_cast<__bf16>(0.01f * float((lane * 7 + st + 2 * e) & 15));
-      kf[st][e] = static_cast<__bf16>(0.01f * float((lane + 3 * st + e) & 15));
-      kg[st][e] = static_cast<__bf16>(0.01f * float((lane + 5 * st + 3 * e) & 15));
+      const uint32_t i = r0 + 8 * st + e;
+      qf[st][e] = seed ? rand_bf16(seed, i) : static_cast<__bf16>(0.01f * float((lane * 7 + st + 2 * e) & 15));
+      kf[st][e] = seed ? rand_bf16(seed, i + 64) : static_cast<__bf16>(0.01f * float((lane + 3 * st + e) & 15));
+      kg[st][e] = seed ? rand_bf16(seed, i + 128) : static_cast<__bf16>(0.01f * float((lane + 5 * st + 3 * e) & 15));
     }
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vf[m][e] = static_cast<__bf16>(0.001f * float((lane + m + e) & 31));
+    for (int e = 0; e < 8; ++e)
+      vf[m][e] = seed ? rand_bf16(seed, r0 + 192 + 8 * m + e) : static_cast<__bf16>(0.001f * float((lane + m + e) & 31));
   // the kernel's LDS operand offsets (permuted K rows, transposing V reads)
   int koff[8], voff[8];
   {
@@ -129,8 +161,11 @@ __global__ __launch_bounds__(256, 2) void calib_tile_kernel(int32_t iters, float
   const unsigned char* kbase = src + kvh * kTileD * 2;
   const unsigned char* vbase = kbase + int64_t(n_tiles) * kKeyTile * kTileRowStride;
   if constexpr (VAR == 1) {
-    for (int i = int(threadIdx.x); i < G::kStageBytes / 4; i += 256)
-      reinterpret_cast<uint32_t*>(lds)[i] = 0x3c003c00u ^ uint32_t(i & 0xff);
+    for (int i = int(threadIdx.x); i < G::kStageBytes / 4; i += 256) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, rand_bf16(seed, 2 * i));
+      const uint32_t hi = __builtin_bit_cast(uint16_t, rand_bf16(seed, 2 * i + 1));
+      reinterpret_cast<uint32_t*>(lds)[i] = seed ? lo | (hi << 16) : 0x3c003c00u ^ uint32_t(i & 0xff);
+    }
   }
   if constexpr (VAR == 2) {
     const int64_t off = int64_t(tile0 % n_tiles) * kKeyTile * kTileRowStride;
@@ -226,16 +261,17 @@ __global__ __launch_bounds__(256, 2) void calib_tile_kernel(int32_t iters, float
 
 }  // namespace
 
-hipError_t launch_calib_tile(int32_t variant, int32_t blocks, int32_t iters, const void* src, int64_t src_bytes,
-                             float* sink, hipStream_t st) {
+hipError_t launch_calib_tile(int32_t variant, int32_t blocks, int32_t iters, uint32_t seed, const void* src,
+                             int64_t src_bytes, float* sink, hipStream_t st) {
   const unsigned char* s8 = static_cast<const unsigned char*>(src);
   const int32_t n_tiles = int32_t(std::min<int64_t>(src_bytes / (2 * kKeyTile * kTileRowStride), 1 << 20));
   if (variant == 0)
-    hipLaunchKernelGGL(calib_tile_kernel<0>, dim3(unsigned(blocks)), dim3(256), 0, st, iters, sink, s8, 1);
+    hipLaunchKernelGGL(calib_tile_kernel<0>, dim3(unsigned(blocks)), dim3(256), 0, st, iters, seed, sink, s8, 1);
   else if (variant == 1)
-    hipLaunchKernelGGL(calib_tile_kernel<1>, dim3(unsigned(blocks)), dim3(256), 0, st, iters, sink, s8, 1);
+    hipLaunchKernelGGL(calib_tile_kernel<1>, dim3(unsigned(blocks)), dim3(256), 0, st, iters, seed, sink, s8, 1);
   else
-    hipLaunchKernelGGL(calib_tile_kernel<2>, dim3(unsigned(blocks)), dim3(256), 0, st, iters, sink, s8, n_tiles);
+    hipLaunchKernelGGL(calib_tile_kernel<2>, dim3(unsigned(blocks)), dim3(256), 0, st, iters, seed, sink, s8,
+                       n_tiles);
   return hipGetLastError();
 }
 
@@ -245,8 +281,8 @@ int64_t calib_tile_flops(int32_t blocks, int32_t iters) {
 
 int64_t calib_tile_min_bytes() { return 2 * kKeyTile * kTileRowStride; }
 
-hipError_t launch_calib_mfma(int32_t blocks, int32_t iters, float* sink, hipStream_t st) {
-  hipLaunchKernelGGL(calib_mfma_kernel, dim3(unsigned(blocks)), dim3(kCalibThreads), 0, st, iters, sink);
+hipError_t launch_calib_mfma(int32_t blocks, int32_t iters, uint32_t seed, float* sink, hipStream_t st) {
+  hipLaunchKernelGGL(calib_mfma_kernel, dim3(unsigned(blocks)), dim3(kCalibThreads), 0, st, iters, seed, sink);
   return hipGetLastError();
 }
 

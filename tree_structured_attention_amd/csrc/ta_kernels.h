@@ -96,11 +96,11 @@ hipError_t launch_accept(int dtype, const AcceptParams& p, int64_t n_rows, hipSt
 // Device address of the file-scope scratch (TA_STATIC_SCRATCH_BYTES) on the
 // current device, looked up on the first call per device.
 hipError_t static_scratch(void** ptr);
-hipError_t launch_calib_mfma(int32_t blocks, int32_t iters, float* sink, hipStream_t st);
+hipError_t launch_calib_mfma(int32_t blocks, int32_t iters, uint32_t seed, float* sink, hipStream_t st);
 hipError_t launch_calib_read(const void* src, int64_t bytes, int32_t blocks, uint32_t* sink, hipStream_t st);
 int64_t calib_mfma_flops(int32_t blocks, int32_t iters);
-hipError_t launch_calib_tile(int32_t variant, int32_t blocks, int32_t iters, const void* src, int64_t src_bytes,
-                             float* sink, hipStream_t st);
+hipError_t launch_calib_tile(int32_t variant, int32_t blocks, int32_t iters, uint32_t seed, const void* src,
+                             int64_t src_bytes, float* sink, hipStream_t st);
 int64_t calib_tile_flops(int32_t blocks, int32_t iters);
 int64_t calib_tile_min_bytes();
 
